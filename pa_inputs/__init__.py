@@ -1,0 +1,295 @@
+"""Seeded synthetic inputs for paged-KV attention.
+
+This module only *draws and lays out* data: random values, sequence lengths,
+block tables and pool sizes.  It holds none of the attention arithmetic, so
+both the fp64 oracle and the HIP path can consume its output without sharing
+any computation.
+
+Storage formats (numpy, host memory):
+
+* ``"f32"``  -- float32 arrays.
+* ``"bf16"`` -- uint16 arrays holding bfloat16 bit patterns (numpy has no
+  bfloat16); values are N(0,1) float32 samples rounded to nearest-even by
+  torch's CPU cast.
+* ``"fp8"``  -- uint8 arrays of OCP FP8 E4M3 ("e4m3fn") codes with one float32
+  scale per (K or V, kv head): ``scale = amax / 448`` and
+  ``code = e4m3(clamp(x / scale, -448, 448))`` via torch's CPU cast.
+
+Pool layout: ``pool[num_blocks][num_kv_heads][block_size][head_dim]``; a
+block table row lists, in logical order, the physical block ids of one
+request ("a small table remembers which blocks belong to which request and in
+what order": "How does TensorRT-LLM work", outcomeschool.com, section "The
+paged KV cache").  Table entries past ``ceil(L / block_size)`` are set to -1
+because they must never be read.
+
+The five named workloads reproduce the Llama-3-8B decode shapes (32 query
+heads, 8 KV heads, head_dim 128: "TensorRT-LLM, in depth", aicassindra.com,
+section "First principles: where the GPU memory goes").  Seeds are
+``1000 + workload number``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+FP8_MAX = 448.0
+
+
+@dataclasses.dataclass
+class Workload:
+    """One batch of inputs for a paged-attention call (host numpy arrays)."""
+
+    name: str
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    q_fmt: str                     # "f32" | "bf16"
+    kv_fmt: str                    # "f32" | "bf16" | "fp8"
+    q: np.ndarray                  # [total_q, Hq, D] in q_fmt storage
+    k_pool: np.ndarray             # [num_blocks, Hkv, bs, D] in kv_fmt storage
+    v_pool: np.ndarray
+    block_table: np.ndarray        # int32 [B, max_blocks_per_seq]
+    seq_lens: np.ndarray           # int32 [B], KV tokens incl. the row's new ones
+    q_lens: np.ndarray             # int32 [B], 1 for decode rows
+    k_scale: Optional[np.ndarray] = None   # float32 [Hkv] (fp8 only)
+    v_scale: Optional[np.ndarray] = None
+    scale: float = 0.0             # softmax scale; 1/sqrt(D) unless stated
+    num_decode_rows: int = 0
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+    @property
+    def q_start_loc(self) -> np.ndarray:
+        out = np.zeros(self.num_seqs + 1, dtype=np.int32)
+        np.cumsum(self.q_lens, out=out[1:])
+        return out
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q_lens.sum())
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.num_seqs else 0
+
+    @property
+    def is_decode_only(self) -> bool:
+        return bool(np.all(self.q_lens == 1))
+
+
+# ----------------------------------------------------------------------------
+# value formats (storage only: rounding of random samples to the stored type)
+# ----------------------------------------------------------------------------
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> uint16 bfloat16 bit patterns, round-to-nearest-even (torch CPU cast)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def quantize_fp8_per_head(x: np.ndarray):
+    """Quantise ``x[..., Hkv, bs, D]`` (pool layout) to E4M3 codes with one scale per kv head.
+
+    Returns ``(codes uint8, scales float32[Hkv])``.
+    """
+    import torch
+    hkv = x.shape[1]
+    amax = np.abs(x).reshape(x.shape[0], hkv, -1).max(axis=(0, 2)).astype(np.float32)
+    amax = np.where(amax > 0, amax, np.float32(1.0))
+    scales = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    y = x / scales[None, :, None, None]
+    y = np.clip(y, -FP8_MAX, FP8_MAX).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scales
+
+
+def _normal(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def _store(x: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if fmt == "bf16":
+        return to_bf16_bits(x)
+    raise ValueError(fmt)
+
+
+# ----------------------------------------------------------------------------
+# block tables
+# ----------------------------------------------------------------------------
+
+def blocks_needed(seq_lens: np.ndarray, block_size: int) -> np.ndarray:
+    return (seq_lens.astype(np.int64) + block_size - 1) // block_size
+
+
+def random_block_table(rng: np.random.Generator, seq_lens: np.ndarray, block_size: int,
+                       num_blocks: int, max_blocks_per_seq: Optional[int] = None) -> np.ndarray:
+    """Hand each row its blocks from a seeded random permutation of the pool.
+
+    Distinct rows get distinct physical blocks; entries past a row's last
+    block are -1.
+    """
+    need = blocks_needed(seq_lens, block_size)
+    total = int(need.sum())
+    if total > num_blocks:
+        raise ValueError(f"pool of {num_blocks} blocks < {total} needed")
+    mb = int(need.max()) if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    mb = max(mb, 1)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    table = np.full((len(seq_lens), mb), -1, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[pos:pos + n]
+        pos += int(n)
+    return table
+
+
+# ----------------------------------------------------------------------------
+# generic generator
+# ----------------------------------------------------------------------------
+
+def make_workload(*, name: str, seq_lens, q_lens=None, num_q_heads=32, num_kv_heads=8,
+                  head_dim=128, block_size=16, q_fmt="bf16", kv_fmt="bf16",
+                  pool_factor: float = 1.0, extra_blocks: int = 0, seed: int = 0,
+                  poison_unused: bool = False, max_blocks_per_seq: Optional[int] = None,
+                  scale: Optional[float] = None) -> Workload:
+    """Draw one workload.
+
+    ``seq_lens[b]`` counts every cached token of row b including its
+    ``q_lens[b]`` new ones.  The pool holds ``ceil(pool_factor * needed) +
+    extra_blocks`` blocks.  With ``poison_unused`` every pool slot no row
+    references (unreferenced blocks and slots past L in a row's last block)
+    is NaN (fp8: code 0x7F).
+    """
+    rng = np.random.default_rng(seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(seq_lens)
+    q_lens = np.ones(B, dtype=np.int32) if q_lens is None else np.asarray(q_lens, dtype=np.int32)
+    if np.any(q_lens < 1) or np.any(q_lens > seq_lens):
+        raise ValueError("need 1 <= q_len <= seq_len")
+    need = int(blocks_needed(seq_lens, block_size).sum())
+    num_blocks = int(np.ceil(pool_factor * need)) + int(extra_blocks)
+    num_blocks = max(num_blocks, 1)
+    table = random_block_table(rng, seq_lens, block_size, num_blocks, max_blocks_per_seq)
+
+    total_q = int(q_lens.sum())
+    q = _store(_normal(rng, (total_q, num_q_heads, head_dim)), q_fmt)
+
+    kshape = (num_blocks, num_kv_heads, block_size, head_dim)
+    kf = _normal(rng, kshape)
+    vf = _normal(rng, kshape)
+    k_scale = v_scale = None
+    if kv_fmt == "fp8":
+        k_pool, k_scale = quantize_fp8_per_head(kf)
+        v_pool, v_scale = quantize_fp8_per_head(vf)
+    else:
+        k_pool, v_pool = _store(kf, kv_fmt), _store(vf, kv_fmt)
+    del kf, vf
+
+    w = Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                 head_dim=head_dim, block_size=block_size, q_fmt=q_fmt, kv_fmt=kv_fmt,
+                 q=q, k_pool=k_pool, v_pool=v_pool, block_table=table, seq_lens=seq_lens,
+                 q_lens=q_lens, k_scale=k_scale, v_scale=v_scale,
+                 scale=(1.0 / np.sqrt(head_dim)) if scale is None else float(scale),
+                 num_decode_rows=leading_decode_rows(q_lens))
+    if poison_unused:
+        poison_pool(w)
+    return w
+
+
+def leading_decode_rows(q_lens: np.ndarray) -> int:
+    """Number of leading rows with q_len == 1 (decode rows come first in a mixed batch)."""
+    big = np.nonzero(np.asarray(q_lens) != 1)[0]
+    return int(big[0]) if len(big) else int(len(q_lens))
+
+
+def poison_mask(w: Workload) -> np.ndarray:
+    """bool [num_blocks, bs]: True where no row's first seq_len tokens live."""
+    used = np.zeros((w.num_blocks, w.block_size), dtype=bool)
+    bs = w.block_size
+    for b in range(w.num_seqs):
+        L = int(w.seq_lens[b])
+        n = (L + bs - 1) // bs
+        for j in range(n):
+            hi = min(bs, L - j * bs)
+            used[w.block_table[b, j], :hi] = True
+    return ~used
+
+
+def poison_pool(w: Workload) -> None:
+    """Overwrite every unreferenced pool slot with NaN (fp8: code 0x7F)."""
+    m = poison_mask(w)
+    nan = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "fp8": np.uint8(0x7F)}[w.kv_fmt]
+    for pool in (w.k_pool, w.v_pool):
+        view = pool.transpose(0, 2, 1, 3)          # [nb, bs, Hkv, D]
+        view[m] = nan
+
+
+# ----------------------------------------------------------------------------
+# the five named workloads
+# ----------------------------------------------------------------------------
+
+WORKLOAD_NAMES = {
+    1: "decode fp32 B1 ctx512 bs16",
+    2: "decode bf16 B32 ctxU[1,4096] bs16 pool2x",
+    3: "decode bf16 B55 ctx8192 bs64",
+    4: "decode fp8kv B128 ctxlogU[128,8192] bs16",
+    5: "mixed bf16 8x256-chunk prefill + 96 decode bs16",
+}
+
+
+def workload_lengths(i: int, seed: Optional[int] = None):
+    """(seq_lens, q_lens) of named workload i, drawn from its own seeded stream."""
+    rng = np.random.default_rng((1000 + i) if seed is None else seed)
+    if i == 1:
+        return np.array([512], np.int32), np.array([1], np.int32)
+    if i == 2:
+        L = rng.integers(1, 4096 + 1, size=32).astype(np.int32)
+        return L, np.ones(32, np.int32)
+    if i == 3:
+        return np.full(55, 8192, np.int32), np.ones(55, np.int32)
+    if i == 4:
+        u = rng.uniform(np.log(128.0), np.log(8192.0), size=128)
+        L = np.clip(np.rint(np.exp(u)), 128, 8192).astype(np.int32)
+        return L, np.ones(128, np.int32)
+    if i == 5:
+        dec = rng.integers(256, 8192 + 1, size=96).astype(np.int32)
+        prior = rng.integers(0, 2048 + 1, size=8).astype(np.int32)
+        L = np.concatenate([dec, prior + 256]).astype(np.int32)
+        ql = np.concatenate([np.ones(96, np.int32), np.full(8, 256, np.int32)])
+        return L, ql
+    raise ValueError(i)
+
+
+def make_config(i: int, seed: Optional[int] = None, poison_unused: bool = False) -> Workload:
+    """Named workload i (1..5) at full size."""
+    seed = (1000 + i) if seed is None else seed
+    L, ql = workload_lengths(i, seed)
+    common = dict(name=WORKLOAD_NAMES[i], seq_lens=L, q_lens=ql, seed=seed + 7919,
+                  poison_unused=poison_unused)
+    if i == 1:
+        return make_workload(block_size=16, q_fmt="f32", kv_fmt="f32", **common)
+    if i == 2:
+        return make_workload(block_size=16, pool_factor=2.0, **common)
+    if i == 3:
+        return make_workload(block_size=64, **common)
+    if i == 4:
+        return make_workload(block_size=16, kv_fmt="fp8", **common)
+    if i == 5:
+        return make_workload(block_size=16, **common)
+    raise ValueError(i)
