@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV decode attention path on one MI355X.
+
+One step = one call of the library on one batch of synthetic inputs already
+resident in HBM: the split-K decode kernel followed by the log-sum-exp merge
+(or, for the mixed workload, the prefill-chunk kernel plus both decode
+kernels).  The default workload is the long-context decode batch: 55 rows at
+8,192 cached tokens, Llama-3-8B GQA shapes (32 q heads, 8 KV heads, head_dim
+128), bf16, 64-token blocks -- one layer of the 55-request example on the
+"TensorRT-LLM, in depth" page (section "First principles: where the GPU
+memory goes").
+
+Prints ONE JSON line.  `value` is the decode-attention KV bandwidth: the
+algorithmic KV bytes of one step divided by the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention KV GB/s and % of HBM peak; tokens/s per layer at Llama-3-8B GQA"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
+                    help="named workload (3 = 55 x 8192 bf16 decode, the headline)")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the oracle baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, gpu_out, budget_s):
+    """Time the fp64 oracle on whole rows of the same workload, one row at a time."""
+    import numpy as np
+    import oracle
+    from paged_kv_attention_13_amd import accounting
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rows = []
+    errs = []
+    t_total = 0.0
+    order = np.random.default_rng(0).permutation(w.num_seqs)
+    for b in order:
+        t0 = time.perf_counter()
+        ref = oracle.paged_attention_row(w, int(b))
+        t_total += time.perf_counter() - t0
+        rows.append(int(b))
+        a = int(w.q_start_loc[b])
+        errs.append(float(np.abs(gpu_out[a:a + ref.shape[0]] - ref).max()))
+        if t_total >= budget_s:
+            break
+    kv = accounting.kv_bytes(w.seq_lens[rows], w.num_kv_heads, w.head_dim, w.kv_fmt)
+    tokens = int(w.seq_lens[rows].sum())
+    return {
+        "value": kv / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {w.num_seqs} rows ({tokens} cached tokens, {kv} KV bytes) of the "
+                  f"same workload, one row at a time, fp64 numpy; {t_total:.2f} s",
+        "kv_tokens_per_s": tokens / t_total,
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "max_abs_err_vs_gpu": max(errs),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU (attention over the paged KV cache needs "
+              "no exchange between GPUs; see the sharding note in the design document); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import pa_inputs
+    from paged_kv_attention_13_amd import accounting, binding
+    from paged_kv_attention_13_amd.device import to_device
+
+    t_gen = time.perf_counter()
+    w = pa_inputs.make_config(args.workload)
+    d = to_device(w)
+    gen_s = time.perf_counter() - t_gen
+    mixed = not w.is_decode_only
+    out = torch.empty(d["q"].shape, dtype=d["q"].dtype, device="cuda")
+
+    if mixed:
+        n_dec = w.num_decode_rows
+        m = binding.make_mixed_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                    d["q_start_loc"], w.scale, num_decode_rows=n_dec,
+                                    max_q_len=int(w.q_lens[n_dec:].max()), max_seq_len=w.max_seq_len,
+                                    out=out, partition_size=args.partition_size)
+        nbytes = binding.mixed_workspace_bytes(m)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        m.base.workspace, m.base.workspace_bytes = ws.data_ptr(), ws.numel()
+        dec = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                       w.scale, max_seq_len=w.max_seq_len, out=out,
+                                       partition_size=args.partition_size)
+        dec.num_seqs = n_dec
+        pl = binding.plan(dec)
+        step = lambda: binding.mixed_args_call(m)  # noqa: E731
+        stages = None
+    else:
+        a = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                     w.scale, max_seq_len=w.max_seq_len, k_scale=d["k_scale"],
+                                     v_scale=d["v_scale"], out=out, partition_size=args.partition_size)
+        pl = binding.plan(a)
+        ws = torch.empty(max(pl.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        stages = (lambda: binding.decode_partials(a), lambda: binding.merge_partials(a))
+        step = None
+
+    def run_step(evs=None):
+        if stages is None:
+            if evs:
+                evs[0].record()
+            step()
+            if evs:
+                evs[1].record()
+                evs[2].record()
+        else:
+            if evs:
+                evs[0].record()
+            stages[0]()
+            if evs:
+                evs[1].record()
+            stages[1]()
+            if evs:
+                evs[2].record()
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    m_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    kernel_ms = float(np.mean(k_ms))
+
+    cb = accounting.workload_bytes(w)
+    kv_bytes = cb["kv"]
+    # algorithmic bytes of the split-K kernel (one launch): KV + scales + q + block table
+    # entries + seq_lens; the output is written by the merge kernel
+    split_bytes = cb["kv"] + cb["scales"] + cb["q"] + cb["meta"]
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = split_bytes / (kernel_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_kernel (split-K partials)" if not mixed else "pa_mixed call (all kernels)",
+                "kernel_ms_mean": round(kernel_ms, 5), "kernel_ms_p10": round(float(np.percentile(k_ms, 10)), 5),
+                "kernel_ms_p90": round(float(np.percentile(k_ms, 90)), 5),
+                "merge_ms_mean": round(float(np.mean(m_ms)), 5),
+                "bytes_per_launch": int(split_bytes)}
+    flops = accounting.call_flops(w.seq_lens, w.q_lens, w.num_q_heads, w.head_dim)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 kv, bf16 q"}[w.kv_fmt] if w.kv_fmt != "bf16" else "bf16",
+        "data": "synthetic (seeded N(0,1) values, random block tables)",
+        "config": {"workload": w.name, "batch": w.num_seqs, "total_q": w.total_q,
+                   "context_tokens": int(w.seq_lens.sum()), "max_context": w.max_seq_len,
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "kv_dtype": w.kv_fmt,
+                   "partition_size": pl.partition_size, "num_partitions": pl.num_partitions},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
+        "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_per_step * 1e-3), 1),
+        "kv_bytes_per_step": int(kv_bytes),
+        "algorithmic_flops_per_step": int(flops),
+        "roofline": roofline,
+        "input_generation_s": round(gen_s, 2),
+    }
+    if args.cpu_seconds > 0:
+        gpu_out = out.float().cpu().numpy().astype(np.float64)
+        res["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

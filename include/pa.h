@@ -1,0 +1,181 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-KV attention library.
+ *
+ * The library computes softmax attention of new query tokens against a KV
+ * cache kept in a pool of equal fixed-size blocks, each request reaching its
+ * tokens through an ordered block table:
+ *   - the pool of equal blocks handed out on demand, and the small table that
+ *     records which blocks belong to which request and in what order:
+ *     "How does TensorRT-LLM work" (outcomeschool.com), section
+ *     "The paged KV cache";
+ *   - virtual-to-physical block tables over non-contiguous blocks:
+ *     "Introduction to TensorRT-LLM" (dileepadev.github.io), section
+ *     "2. Paged KV Cache";
+ *   - each decode step reads the request's entire KV cache and is therefore
+ *     memory-bandwidth-bound; grouped-query attention with 8 KV heads for
+ *     Llama-3-8B: "TensorRT-LLM, in depth" (aicassindra.com), section
+ *     "First principles: where the GPU memory goes";
+ *   - prefill chunks mixed with decode rows in one pass: same page, section
+ *     "In-flight batching and the scheduler";
+ *   - an FP8 KV cache: same page, section "Quantization: fewer bytes per
+ *     weight and per cached token".
+ *
+ * Operation (one layer).  For row b with L = seq_lens[b] cached tokens
+ * (including the row's n new ones), new query i in [0, n), and query head h
+ * of kv head g = h / (Hq / Hkv):
+ *     K[t] = k_pool[block_table[b][t / bs]][g][t % bs][:]      (t < L)
+ *     out[i][h] = sum_t softmax_t(scale * <q[i][h], K[t]>) V[t],
+ *                 over t <= L - n + i (every earlier token and its own).
+ * FP8 pools hold OCP E4M3 codes; the value is code * k_scale[g] (V: v_scale[g]).
+ *
+ * Memory layout (all row-major, densely packed, element strides implied):
+ *     q, out       [rows][Hq][D]            rows = num_seqs (decode) or total_q
+ *     k_pool,v_pool[num_blocks][Hkv][bs][D] one (block, kv head) page contiguous
+ *     block_table  [num_seqs][max_blocks_per_seq] int32
+ *     seq_lens     [num_seqs] int32
+ *     q_start_loc  [num_seqs + 1] int32, exclusive prefix sum of q_len
+ *
+ * Pointers in the argument structs are DEVICE pointers except in the
+ * pa_check_*_metadata calls, which read HOST copies.  The caller owns every
+ * buffer, including the workspace (size from pa_decode_plan /
+ * pa_mixed_workspace_size).  The library keeps no pointer after a call
+ * returns, allocates no memory, and never synchronises: work is queued on
+ * `stream` (a hipStream_t; NULL = the default stream) and the call returns.
+ * Calls are safe to record into a HIP graph.
+ *
+ * Errors.  Every host-checkable problem returns a status before anything is
+ * launched: null pointers, misalignment (16 bytes for q, pools, out,
+ * workspace), dtype combinations, Hq % Hkv, supported head_dim / block size /
+ * group size, workspace too small, num_decode_rows > num_seqs.  Launch
+ * failures return PA_ERR_HIP.  The device-resident metadata is a
+ * PRECONDITION that the kernels do not re-check:
+ *     1 <= q_len_b <= L_b <= max_seq_len <= max_blocks_per_seq * bs,
+ *     0 <= block_table[b][j] < num_blocks for j < ceil(L_b / bs).
+ * pa_check_decode_metadata / pa_check_mixed_metadata verify it on host copies.
+ * Table entries at j >= ceil(L_b / bs), pool slots past L_b in a row's last
+ * block and blocks no row references are never read into the result.
+ * No C++ exception crosses this interface.  pa_last_error() returns a
+ * thread-local message describing the last non-OK status.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+/* Element types.  Supported (q, kv, out) combinations:
+ *   (F32, F32, F32|BF16), (BF16, BF16, BF16|F32), (BF16, FP8_E4M3, BF16|F32). */
+typedef enum {
+  PA_F32 = 0,
+  PA_BF16 = 1,
+  PA_FP8_E4M3 = 2
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,
+  PA_ERR_BAD_SHAPE = 2,
+  PA_ERR_BAD_DTYPE = 3,
+  PA_ERR_UNSUPPORTED = 4,
+  PA_ERR_WORKSPACE_TOO_SMALL = 5,
+  PA_ERR_MISALIGNED = 6,
+  PA_ERR_BAD_METADATA = 7,
+  PA_ERR_HIP = 8
+} pa_status;
+
+/* Arguments of a decode call: one new query token per row. */
+typedef struct pa_decode_args {
+  int32_t num_seqs;            /* B >= 0 rows */
+  int32_t num_q_heads;         /* Hq, multiple of num_kv_heads; Hq/Hkv in {1,2,4,8} */
+  int32_t num_kv_heads;        /* Hkv >= 1 */
+  int32_t head_dim;            /* D; 128 is supported */
+  int32_t block_size;          /* bs: tokens per block, one of 16, 32, 64, 128 */
+  int32_t num_blocks;          /* physical blocks in each pool */
+  int32_t max_blocks_per_seq;  /* row stride of block_table */
+  int32_t max_seq_len;         /* host-known upper bound on seq_lens (grid planning) */
+  int32_t partition_size;      /* split-K partition in tokens (multiple of 128, at most
+                                  64 * bs); 0 = the library chooses */
+  int32_t q_dtype;             /* pa_dtype */
+  int32_t kv_dtype;            /* pa_dtype */
+  int32_t out_dtype;           /* pa_dtype */
+  const void *q;               /* [B][Hq][D] */
+  const void *k_pool;          /* [num_blocks][Hkv][bs][D] */
+  const void *v_pool;          /* [num_blocks][Hkv][bs][D] */
+  const float *k_scale;        /* [Hkv], required iff kv_dtype == PA_FP8_E4M3, else NULL */
+  const float *v_scale;        /* [Hkv], same rule */
+  const int32_t *block_table;  /* [B][max_blocks_per_seq] */
+  const int32_t *seq_lens;     /* [B], tokens in cache including the new one, >= 1 */
+  float scale;                 /* softmax scale (1/sqrt(D) for standard attention) */
+  void *out;                   /* [B][Hq][D], out_dtype */
+  void *workspace;             /* split-K partials; may be NULL when the plan needs 0 bytes */
+  size_t workspace_bytes;
+} pa_decode_args;
+
+/* Arguments of a mixed in-flight batch: rows [0, num_decode_rows) are decode
+ * rows (q_len 1), the remaining rows are chunked-prefill rows whose q_len new
+ * tokens are already appended to the cache. */
+typedef struct pa_mixed_args {
+  pa_decode_args base;         /* base.q and base.out are [total_q][Hq][D];
+                                  base.seq_lens counts the row's new tokens too */
+  const int32_t *q_start_loc;  /* [num_seqs + 1] */
+  int32_t total_q;             /* q_start_loc[num_seqs] */
+  int32_t num_decode_rows;     /* rows with q_len == 1 placed first */
+  int32_t max_q_len;           /* host-known upper bound on prefill-row q_len */
+} pa_mixed_args;
+
+/* Launch plan of a decode call. */
+typedef struct pa_plan {
+  int32_t partition_size;      /* tokens per split-K partition */
+  int32_t num_partitions;      /* partitions per row (from max_seq_len) */
+  size_t workspace_bytes;      /* 0 when num_partitions == 1 */
+} pa_plan;
+
+int pa_abi_version(void);
+
+/* Validate host-visible arguments and compute the split-K plan.  The plan is
+ * a pure function of (num_seqs, Hq, Hkv, block_size, max_seq_len,
+ * partition_size) and the device's compute-unit count. */
+pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
+
+/* Workspace bytes a pa_mixed call needs (its decode rows' split-K partials). */
+pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes);
+
+/* Decode attention over the paged cache: split-K partial kernel followed, when
+ * the plan has more than one partition, by the log-sum-exp merge kernel.  Both
+ * are queued on `stream`. */
+pa_status pa_decode(const pa_decode_args *a, void *stream);
+
+/* The two stages of pa_decode, callable separately (e.g. to time one, or to
+ * merge partials gathered from elsewhere).  pa_decode_partials writes, for
+ * every (row, q head, partition), the partition's running max m (log2
+ * domain), its sum l of exp2(s - m) and the unnormalised sum of exp2(s - m) V
+ * into the workspace; pa_merge_partials combines them into `out`.  With a
+ * one-partition plan pa_decode_partials writes `out` directly and
+ * pa_merge_partials does nothing. */
+pa_status pa_decode_partials(const pa_decode_args *a, void *stream);
+pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
+
+/* Mixed in-flight batch: decode rows through the split-K decode kernels,
+ * prefill-chunk rows through the MFMA causal tile kernel, all on `stream`. */
+pa_status pa_mixed(const pa_mixed_args *a, void *stream);
+
+/* Synchronous CPU validation of the metadata preconditions above.  The
+ * pointers block_table, seq_lens (and q_start_loc) must be HOST pointers;
+ * q/pool/out pointers are not read. */
+pa_status pa_check_decode_metadata(const pa_decode_args *a_host);
+pa_status pa_check_mixed_metadata(const pa_mixed_args *a_host);
+
+const char *pa_status_string(pa_status s);
+const char *pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

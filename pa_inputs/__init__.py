@@ -30,6 +30,7 @@ section "First principles: where the GPU memory goes").  Seeds are
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -107,18 +108,41 @@ def quantize_fp8_per_head(x: np.ndarray):
     Returns ``(codes uint8, scales float32[Hkv])``.
     """
     import torch
-    hkv = x.shape[1]
-    amax = np.abs(x).reshape(x.shape[0], hkv, -1).max(axis=(0, 2)).astype(np.float32)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    amax = t.abs().amax(dim=(0, 2, 3)).numpy().astype(np.float32)
     amax = np.where(amax > 0, amax, np.float32(1.0))
     scales = (amax / np.float32(FP8_MAX)).astype(np.float32)
-    y = x / scales[None, :, None, None]
-    y = np.clip(y, -FP8_MAX, FP8_MAX).astype(np.float32)
-    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    y = t / torch.from_numpy(scales)[None, :, None, None]
+    y = y.clamp_(-FP8_MAX, FP8_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     return codes, scales
 
 
-def _normal(rng: np.random.Generator, shape) -> np.ndarray:
-    return rng.standard_normal(size=shape, dtype=np.float32)
+def _normal(seed_seq: np.random.SeedSequence, shape) -> np.ndarray:
+    """N(0,1) float32 samples of ``shape``, filled in fixed 4 Mi-element chunks.
+
+    Chunk i draws from ``default_rng(seed_seq.spawn(...)[i])``, so the result
+    depends only on (seed, shape), not on how many threads fill it.
+    """
+    out = np.empty(shape, dtype=np.float32)
+    flat = out.reshape(-1)
+    n = flat.size
+    chunk = 1 << 22
+    children = seed_seq.spawn(max(1, (n + chunk - 1) // chunk))
+
+    def fill(i):
+        a = i * chunk
+        b = min(n, a + chunk)
+        np.random.default_rng(children[i]).standard_normal(size=b - a, dtype=np.float32, out=flat[a:b])
+
+    if len(children) == 1:
+        fill(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        workers = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 4)
+        with ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+            list(ex.map(fill, range(len(children))))
+    return out
 
 
 def _store(x: np.ndarray, fmt: str) -> np.ndarray:
@@ -176,7 +200,8 @@ def make_workload(*, name: str, seq_lens, q_lens=None, num_q_heads=32, num_kv_he
     references (unreferenced blocks and slots past L in a row's last block)
     is NaN (fp8: code 0x7F).
     """
-    rng = np.random.default_rng(seed)
+    ss_table, ss_q, ss_k, ss_v = np.random.SeedSequence(seed).spawn(4)
+    rng = np.random.default_rng(ss_table)
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = len(seq_lens)
     q_lens = np.ones(B, dtype=np.int32) if q_lens is None else np.asarray(q_lens, dtype=np.int32)
@@ -188,11 +213,11 @@ def make_workload(*, name: str, seq_lens, q_lens=None, num_q_heads=32, num_kv_he
     table = random_block_table(rng, seq_lens, block_size, num_blocks, max_blocks_per_seq)
 
     total_q = int(q_lens.sum())
-    q = _store(_normal(rng, (total_q, num_q_heads, head_dim)), q_fmt)
+    q = _store(_normal(ss_q, (total_q, num_q_heads, head_dim)), q_fmt)
 
     kshape = (num_blocks, num_kv_heads, block_size, head_dim)
-    kf = _normal(rng, kshape)
-    vf = _normal(rng, kshape)
+    kf = _normal(ss_k, kshape)
+    vf = _normal(ss_v, kshape)
     k_scale = v_scale = None
     if kv_fmt == "fp8":
         k_pool, k_scale = quantize_fp8_per_head(kf)

@@ -1,0 +1,299 @@
+"""ctypes binding of ``libpa_kv.so`` (the C ABI declared in ``include/pa.h``).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+the current HIP stream, outputs and workspaces are allocated with torch, and
+the call goes straight to the library.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback.  If the library is not
+built, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpa_kv.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
+                4: "PA_ERR_UNSUPPORTED", 5: "PA_ERR_WORKSPACE_TOO_SMALL", 6: "PA_ERR_MISALIGNED",
+                7: "PA_ERR_BAD_METADATA", 8: "PA_ERR_HIP"}
+
+EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_decode",
+            "pa_decode_partials", "pa_merge_partials", "pa_mixed", "pa_check_decode_metadata",
+            "pa_check_mixed_metadata", "pa_status_string", "pa_last_error"]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("partition_size", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class MixedArgs(ctypes.Structure):
+    _fields_ = [
+        ("base", DecodeArgs),
+        ("q_start_loc", ctypes.c_void_p),
+        ("total_q", ctypes.c_int32),
+        ("num_decode_rows", ctypes.c_int32),
+        ("max_q_len", ctypes.c_int32),
+    ]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("partition_size", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message or STATUS_NAMES.get(status, str(status)))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_attention_13_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    sigs = {
+        "pa_abi_version": ([], ctypes.c_int),
+        "pa_decode_plan": ([P(DecodeArgs), P(Plan)], ctypes.c_int),
+        "pa_mixed_workspace_size": ([P(MixedArgs), P(ctypes.c_size_t)], ctypes.c_int),
+        "pa_decode": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_decode_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_merge_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_mixed": ([P(MixedArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_check_decode_metadata": ([P(DecodeArgs)], ctypes.c_int),
+        "pa_check_mixed_metadata": ([P(MixedArgs)], ctypes.c_int),
+        "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "pa_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (argtypes, restype) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    return lib
+
+
+LIB = _load()
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise PagedAttentionError(status, LIB.pa_last_error().decode())
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return PA_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq_len: int,
+                     k_scale=None, v_scale=None, out=None, partition_size: int = 0,
+                     workspace=None) -> DecodeArgs:
+    a = DecodeArgs()
+    a.num_seqs = int(seq_lens.shape[0])
+    a.num_q_heads = int(q.shape[1])
+    a.num_kv_heads = int(k_pool.shape[1])
+    a.head_dim = int(q.shape[2])
+    a.block_size = int(k_pool.shape[2])
+    a.num_blocks = int(k_pool.shape[0])
+    a.max_blocks_per_seq = int(block_table.shape[1])
+    a.max_seq_len = int(max_seq_len)
+    a.partition_size = int(partition_size)
+    a.q_dtype = dtype_code(q)
+    a.kv_dtype = dtype_code(k_pool)
+    a.out_dtype = dtype_code(out) if out is not None else a.q_dtype
+    a.q = _ptr(q)
+    a.k_pool = _ptr(k_pool)
+    a.v_pool = _ptr(v_pool)
+    a.k_scale = _ptr(k_scale)
+    a.v_scale = _ptr(v_scale)
+    a.block_table = _ptr(block_table)
+    a.seq_lens = _ptr(seq_lens)
+    a.scale = float(scale)
+    a.out = _ptr(out)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def plan(args: DecodeArgs) -> Plan:
+    p = Plan()
+    check(LIB.pa_decode_plan(ctypes.byref(args), ctypes.byref(p)))
+    return p
+
+
+def _alloc_out(q, out_dtype):
+    torch = _torch()
+    return torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+
+
+def _alloc_workspace(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq_len: int,
+           k_scale=None, v_scale=None, out=None, out_dtype=None, partition_size: int = 0,
+           workspace=None, stream=None):
+    """Decode attention (``pa_decode``).  Returns ``out`` [B, Hq, D]."""
+    if out is None:
+        out = _alloc_out(q, out_dtype)
+    a = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
+                         k_scale=k_scale, v_scale=v_scale, out=out, partition_size=partition_size)
+    if workspace is None:
+        workspace = _alloc_workspace(plan(a).workspace_bytes, q.device)
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    check(LIB.pa_decode(ctypes.byref(a), ctypes.c_void_p(_stream(stream))))
+    return out
+
+
+def decode_partials(args: DecodeArgs, stream=None) -> None:
+    check(LIB.pa_decode_partials(ctypes.byref(args), ctypes.c_void_p(_stream(stream))))
+
+
+def merge_partials(args: DecodeArgs, stream=None) -> None:
+    check(LIB.pa_merge_partials(ctypes.byref(args), ctypes.c_void_p(_stream(stream))))
+
+
+def decode_args_call(args: DecodeArgs, stream=None) -> None:
+    check(LIB.pa_decode(ctypes.byref(args), ctypes.c_void_p(_stream(stream))))
+
+
+def make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *,
+                    num_decode_rows: int, max_q_len: int, max_seq_len: int, out=None,
+                    partition_size: int = 0) -> MixedArgs:
+    m = MixedArgs()
+    m.base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
+                              out=out, partition_size=partition_size)
+    m.q_start_loc = _ptr(q_start_loc)
+    m.total_q = int(q.shape[0])
+    m.num_decode_rows = int(num_decode_rows)
+    m.max_q_len = int(max_q_len)
+    return m
+
+
+def mixed_workspace_bytes(m: MixedArgs) -> int:
+    n = ctypes.c_size_t()
+    check(LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mixed(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *, num_decode_rows: int,
+          max_q_len: int, max_seq_len: int, out=None, out_dtype=None, partition_size: int = 0,
+          workspace=None, stream=None):
+    """Mixed decode + chunked-prefill batch (``pa_mixed``).  Returns ``out`` [total_q, Hq, D]."""
+    if out is None:
+        out = _alloc_out(q, out_dtype)
+    m = make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale,
+                        num_decode_rows=num_decode_rows, max_q_len=max_q_len,
+                        max_seq_len=max_seq_len, out=out, partition_size=partition_size)
+    if workspace is None:
+        workspace = _alloc_workspace(mixed_workspace_bytes(m), q.device)
+    if workspace is not None:
+        m.base.workspace = _ptr(workspace)
+        m.base.workspace_bytes = workspace.numel() * workspace.element_size()
+    check(LIB.pa_mixed(ctypes.byref(m), ctypes.c_void_p(_stream(stream))))
+    return out
+
+
+def mixed_args_call(m: MixedArgs, stream=None) -> None:
+    check(LIB.pa_mixed(ctypes.byref(m), ctypes.c_void_p(_stream(stream))))
+
+
+def check_decode_metadata(block_table, seq_lens, *, num_q_heads: int, num_kv_heads: int,
+                          head_dim: int, block_size: int, num_blocks: int, max_seq_len: int,
+                          q_dtype: int = PA_BF16, kv_dtype: int = PA_BF16) -> None:
+    """Host-side precondition check (``pa_check_decode_metadata``) on numpy int32 arrays."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    a = DecodeArgs()
+    a.num_seqs, a.num_q_heads, a.num_kv_heads = len(sl), num_q_heads, num_kv_heads
+    a.head_dim, a.block_size, a.num_blocks = head_dim, block_size, num_blocks
+    a.max_blocks_per_seq, a.max_seq_len = bt.shape[1], max_seq_len
+    a.q_dtype, a.kv_dtype, a.out_dtype = q_dtype, kv_dtype, q_dtype
+    a.block_table = bt.ctypes.data
+    a.seq_lens = sl.ctypes.data
+    check(LIB.pa_check_decode_metadata(ctypes.byref(a)))
+
+
+def check_mixed_metadata(block_table, seq_lens, q_start_loc, *, num_decode_rows: int, max_q_len: int,
+                         num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                         num_blocks: int, max_seq_len: int) -> None:
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(q_start_loc, dtype=np.int32)
+    m = MixedArgs()
+    a = m.base
+    a.num_seqs, a.num_q_heads, a.num_kv_heads = len(sl), num_q_heads, num_kv_heads
+    a.head_dim, a.block_size, a.num_blocks = head_dim, block_size, num_blocks
+    a.max_blocks_per_seq, a.max_seq_len = bt.shape[1], max_seq_len
+    a.q_dtype = a.kv_dtype = a.out_dtype = PA_BF16
+    a.block_table = bt.ctypes.data
+    a.seq_lens = sl.ctypes.data
+    m.q_start_loc = qs.ctypes.data
+    m.total_q = int(qs[-1])
+    m.num_decode_rows = num_decode_rows
+    m.max_q_len = max_q_len
+    check(LIB.pa_check_mixed_metadata(ctypes.byref(m)))

@@ -1,0 +1,272 @@
+// Host side of the C ABI: argument validation, split-K planning, metadata
+// checks and error reporting.  Plain C++ (no HIP calls) so that it can be
+// built and tested on a machine without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2_block(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+}  // namespace
+
+pa_status set_error(pa_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(pa_status_string(s)) + ": " + buf;
+  return s;
+}
+
+size_t elem_bytes(int dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_BF16: return 2;
+    case PA_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers) {
+  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  if (a->num_seqs < 0) return set_error(PA_ERR_BAD_SHAPE, "num_seqs = %d < 0", a->num_seqs);
+  if (a->num_kv_heads < 1 || a->num_q_heads < 1)
+    return set_error(PA_ERR_BAD_SHAPE, "head counts must be >= 1 (Hq=%d, Hkv=%d)",
+                     a->num_q_heads, a->num_kv_heads);
+  if (a->num_q_heads % a->num_kv_heads != 0)
+    return set_error(PA_ERR_BAD_SHAPE, "Hq=%d is not a multiple of Hkv=%d", a->num_q_heads,
+                     a->num_kv_heads);
+  const int group = a->num_q_heads / a->num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return set_error(PA_ERR_UNSUPPORTED, "group size Hq/Hkv=%d (supported: 1, 2, 4, 8)", group);
+  if (a->head_dim != kHeadDim)
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim=%d (supported: %d)", a->head_dim, kHeadDim);
+  if (!is_pow2_block(a->block_size))
+    return set_error(PA_ERR_UNSUPPORTED, "block_size=%d (supported: 16, 32, 64, 128)",
+                     a->block_size);
+  if (a->num_blocks < 1 || a->max_blocks_per_seq < 1)
+    return set_error(PA_ERR_BAD_SHAPE, "num_blocks=%d, max_blocks_per_seq=%d must be >= 1",
+                     a->num_blocks, a->max_blocks_per_seq);
+  if (a->num_seqs > 0 && a->max_seq_len < 1)
+    return set_error(PA_ERR_BAD_SHAPE, "max_seq_len=%d must be >= 1", a->max_seq_len);
+  if ((int64_t)a->max_seq_len > (int64_t)a->max_blocks_per_seq * a->block_size)
+    return set_error(PA_ERR_BAD_SHAPE, "max_seq_len=%d exceeds max_blocks_per_seq*block_size=%lld",
+                     a->max_seq_len, (long long)a->max_blocks_per_seq * a->block_size);
+  // dtype combinations
+  const bool ok_out = a->out_dtype == PA_F32 || a->out_dtype == PA_BF16;
+  bool ok = ok_out && ((a->q_dtype == PA_F32 && a->kv_dtype == PA_F32) ||
+                       (a->q_dtype == PA_BF16 && a->kv_dtype == PA_BF16) ||
+                       (a->q_dtype == PA_BF16 && a->kv_dtype == PA_FP8_E4M3));
+  if (!ok)
+    return set_error(PA_ERR_BAD_DTYPE,
+                     "unsupported (q, kv, out) dtypes (%d, %d, %d); supported: (f32, f32, f32|bf16), "
+                     "(bf16, bf16, bf16|f32), (bf16, fp8_e4m3, bf16|f32)",
+                     a->q_dtype, a->kv_dtype, a->out_dtype);
+  const bool fp8 = a->kv_dtype == PA_FP8_E4M3;
+  if (!fp8 && (a->k_scale || a->v_scale))
+    return set_error(PA_ERR_BAD_DTYPE, "k_scale/v_scale are only used with an FP8 KV cache");
+  if (a->partition_size != 0) {
+    if (a->partition_size % kPartitionQuantum != 0 ||
+        a->partition_size > kMaxPagesPerPartition * a->block_size)
+      return set_error(PA_ERR_UNSUPPORTED,
+                       "partition_size=%d must be a multiple of %d and at most %d (64 blocks)",
+                       a->partition_size, kPartitionQuantum, kMaxPagesPerPartition * a->block_size);
+  }
+  if (need_device_pointers && a->num_seqs > 0) {
+    if (!a->q || !a->k_pool || !a->v_pool || !a->block_table || !a->seq_lens || !a->out)
+      return set_error(PA_ERR_NULL_POINTER, "q, k_pool, v_pool, block_table, seq_lens and out are required");
+    if (fp8 && (!a->k_scale || !a->v_scale))
+      return set_error(PA_ERR_NULL_POINTER, "an FP8 KV cache needs k_scale and v_scale");
+    if (!aligned16(a->q) || !aligned16(a->k_pool) || !aligned16(a->v_pool) || !aligned16(a->out))
+      return set_error(PA_ERR_MISALIGNED, "q, k_pool, v_pool and out must be 16-byte aligned");
+    if (a->workspace && !aligned16(a->workspace))
+      return set_error(PA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  }
+  return PA_OK;
+}
+
+pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
+  const int bs = a->block_size;
+  const int max_p = kMaxPagesPerPartition * bs;
+  int P = a->partition_size;
+  if (P == 0) {
+    // Choose the largest partition that still yields enough workgroups to
+    // fill the chip: units = rows * kv heads; each unit is split into
+    // ceil(max_seq_len / P) partitions of 4 waves.
+    const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
+    const int64_t target = 4LL * kTargetCUs;   // >= ~4 workgroups per CU
+    P = kPartitionQuantum;
+    for (int cand = max_p; cand >= kPartitionQuantum; cand /= 2) {
+      if (cand % kPartitionQuantum) continue;
+      const int64_t parts = (a->max_seq_len + cand - 1) / cand;
+      if (units * parts >= target || cand == kPartitionQuantum) { P = cand; break; }
+    }
+  }
+  const int S = a->max_seq_len > 0 ? (a->max_seq_len + P - 1) / P : 1;
+  plan->partition_size = P;
+  plan->num_partitions = S;
+  if (S <= 1 || a->num_seqs == 0) {
+    plan->workspace_bytes = 0;
+  } else {
+    const size_t n = (size_t)a->num_seqs * a->num_q_heads * S;
+    plan->workspace_bytes = 2 * round_up(n * sizeof(float), 256) +
+                            round_up(n * kHeadDim * sizeof(float), 256);
+  }
+  return PA_OK;
+}
+
+pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, DecodeLaunch *L) {
+  std::memset(L, 0, sizeof *L);
+  L->q = a->q;
+  L->k_pool = a->k_pool;
+  L->v_pool = a->v_pool;
+  L->k_scale = a->k_scale;
+  L->v_scale = a->v_scale;
+  L->block_table = a->block_table;
+  L->seq_lens = a->seq_lens;
+  L->out = a->out;
+  L->num_seqs = a->num_seqs;
+  L->num_q_heads = a->num_q_heads;
+  L->num_kv_heads = a->num_kv_heads;
+  L->block_size = a->block_size;
+  L->max_blocks_per_seq = a->max_blocks_per_seq;
+  L->partition_size = plan.partition_size;
+  L->num_partitions = plan.num_partitions;
+  L->kv_dtype = a->kv_dtype;
+  L->out_dtype = a->out_dtype;
+  L->scale = a->scale;
+  if (plan.workspace_bytes > 0) {
+    if (!a->workspace || a->workspace_bytes < plan.workspace_bytes)
+      return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, plan needs %zu",
+                       a->workspace ? a->workspace_bytes : (size_t)0, plan.workspace_bytes);
+    const size_t n = (size_t)a->num_seqs * a->num_q_heads * plan.num_partitions;
+    char *base = static_cast<char *>(a->workspace);
+    L->part_m = reinterpret_cast<float *>(base);
+    L->part_l = reinterpret_cast<float *>(base + round_up(n * sizeof(float), 256));
+    L->part_acc = reinterpret_cast<float *>(base + 2 * round_up(n * sizeof(float), 256));
+  }
+  return PA_OK;
+}
+
+namespace {
+
+pa_status check_rows(const pa_decode_args *a, const int32_t *qsl, int n_dec, int max_q_len) {
+  const int bs = a->block_size;
+  for (int b = 0; b < a->num_seqs; ++b) {
+    const int L = a->seq_lens[b];
+    if (L < 1)
+      return set_error(PA_ERR_BAD_METADATA, "seq_lens[%d]=%d < 1", b, L);
+    if (L > a->max_seq_len)
+      return set_error(PA_ERR_BAD_METADATA, "seq_lens[%d]=%d > max_seq_len=%d", b, L, a->max_seq_len);
+    if ((int64_t)L > (int64_t)a->max_blocks_per_seq * bs)
+      return set_error(PA_ERR_BAD_METADATA, "seq_lens[%d]=%d needs more than %d blocks", b, L,
+                       a->max_blocks_per_seq);
+    const int nb = (L + bs - 1) / bs;
+    const int32_t *row = a->block_table + (size_t)b * a->max_blocks_per_seq;
+    for (int j = 0; j < nb; ++j)
+      if (row[j] < 0 || row[j] >= a->num_blocks)
+        return set_error(PA_ERR_BAD_METADATA, "block_table[%d][%d]=%d outside [0, %d)", b, j, row[j],
+                         a->num_blocks);
+    if (qsl) {
+      const int ql = qsl[b + 1] - qsl[b];
+      if (ql < 1 || ql > L)
+        return set_error(PA_ERR_BAD_METADATA, "row %d: q_len=%d outside [1, seq_len=%d]", b, ql, L);
+      if (b < n_dec && (ql != 1 || qsl[b] != b))
+        return set_error(PA_ERR_BAD_METADATA, "decode row %d must have q_len 1 at q index %d", b, b);
+      if (b >= n_dec && ql > max_q_len)
+        return set_error(PA_ERR_BAD_METADATA, "row %d: q_len=%d > max_q_len=%d", b, ql, max_q_len);
+    }
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char *pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL_POINTER: return "PA_ERR_NULL_POINTER";
+    case PA_ERR_BAD_SHAPE: return "PA_ERR_BAD_SHAPE";
+    case PA_ERR_BAD_DTYPE: return "PA_ERR_BAD_DTYPE";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_MISALIGNED: return "PA_ERR_MISALIGNED";
+    case PA_ERR_BAD_METADATA: return "PA_ERR_BAD_METADATA";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char *pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan) {
+  if (!plan) return set_error(PA_ERR_NULL_POINTER, "plan is NULL");
+  pa_status s = validate_decode(a, false);
+  if (s != PA_OK) return s;
+  return plan_decode(a, plan);
+}
+
+pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes) {
+  if (!a || !bytes) return set_error(PA_ERR_NULL_POINTER, "argument is NULL");
+  pa_decode_args d = a->base;
+  if (a->num_decode_rows < 0 || a->num_decode_rows > a->base.num_seqs)
+    return set_error(PA_ERR_BAD_SHAPE, "num_decode_rows=%d outside [0, num_seqs=%d]",
+                     a->num_decode_rows, a->base.num_seqs);
+  d.num_seqs = a->num_decode_rows;
+  pa_status s = validate_decode(&d, false);
+  if (s != PA_OK) return s;
+  pa_plan p;
+  plan_decode(&d, &p);
+  *bytes = p.workspace_bytes;
+  return PA_OK;
+}
+
+pa_status pa_check_decode_metadata(const pa_decode_args *a) {
+  pa_status s = validate_decode(a, false);
+  if (s != PA_OK) return s;
+  if (a->num_seqs > 0 && (!a->seq_lens || !a->block_table))
+    return set_error(PA_ERR_NULL_POINTER, "seq_lens and block_table host copies are required");
+  return check_rows(a, nullptr, 0, 0);
+}
+
+pa_status pa_check_mixed_metadata(const pa_mixed_args *a) {
+  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  pa_status s = validate_decode(&a->base, false);
+  if (s != PA_OK) return s;
+  const int B = a->base.num_seqs;
+  if (B > 0 && (!a->base.seq_lens || !a->base.block_table || !a->q_start_loc))
+    return set_error(PA_ERR_NULL_POINTER, "seq_lens, block_table and q_start_loc host copies are required");
+  if (a->num_decode_rows < 0 || a->num_decode_rows > B)
+    return set_error(PA_ERR_BAD_SHAPE, "num_decode_rows=%d outside [0, %d]", a->num_decode_rows, B);
+  if (B > 0) {
+    if (a->q_start_loc[0] != 0)
+      return set_error(PA_ERR_BAD_METADATA, "q_start_loc[0]=%d != 0", a->q_start_loc[0]);
+    if (a->q_start_loc[B] != a->total_q)
+      return set_error(PA_ERR_BAD_METADATA, "q_start_loc[%d]=%d != total_q=%d", B, a->q_start_loc[B],
+                       a->total_q);
+  }
+  return check_rows(&a->base, a->q_start_loc, a->num_decode_rows, a->max_q_len);
+}
+
+}  // extern "C"

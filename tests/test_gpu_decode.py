@@ -1,0 +1,231 @@
+"""GPU parity of the decode path (pa_decode and its two stages) against the fp64 oracle.
+
+Every case prints its name before running so that a failing GPU step names
+itself.  Inputs are seeded; the oracle never sees anything the GPU produced.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pa_inputs
+from gpu_util import TOL_BF16, TOL_F32, TOL_FP8, compare, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _small(seq_lens, bs=16, kv_fmt="bf16", q_fmt="bf16", hq=32, hkv=8, seed=0, poison=True,
+           extra_blocks=3):
+    return pa_inputs.make_workload(name="small", seq_lens=seq_lens, num_q_heads=hq, num_kv_heads=hkv,
+                                   head_dim=128, block_size=bs, q_fmt=q_fmt, kv_fmt=kv_fmt, seed=seed,
+                                   extra_blocks=extra_blocks, poison_unused=poison)
+
+
+RAGGED = [1, 2, 7, 15, 16, 17, 31, 33, 100, 127, 128, 129, 255, 300, 511, 513, 1000]
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
+@pytest.mark.parametrize("partition_size", [0, 128, 256])
+def test_bf16_ragged_lengths(bs, partition_size):
+    _announce(f"bf16 ragged bs={bs} P={partition_size}")
+    w = _small(RAGGED, bs=bs, seed=bs + partition_size)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, partition_size=partition_size)
+    compare(got, ref, TOL_BF16, what=f"bf16 bs{bs} P{partition_size}")
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_bf16_out_dtypes(out):
+    _announce(f"bf16 kv, out={out}")
+    w = _small([5, 64, 700, 2049], seed=3)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, out_dtype=out)
+    tol = 5e-3 if out == "f32" else TOL_BF16
+    compare(got, ref, tol, what=f"out {out}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (4, 1), (12, 3)])
+def test_group_sizes(hq, hkv):
+    _announce(f"group size hq={hq} hkv={hkv}")
+    w = _small([3, 77, 300, 1100], hq=hq, hkv=hkv, seed=hq * 10 + hkv)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, out_dtype="f32")
+    compare(got, ref, 5e-3, what=f"G={hq // hkv}")
+
+
+def test_fp32_path():
+    _announce("fp32 ragged")
+    w = _small(RAGGED, q_fmt="f32", kv_fmt="f32", seed=11)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w)
+    compare(got, ref, TOL_F32, rel_tol=1e-5, what="fp32")
+
+
+@pytest.mark.parametrize("partition_size", [0, 128, 512])
+def test_fp8_ragged(partition_size):
+    _announce(f"fp8 ragged P={partition_size}")
+    w = _small(RAGGED, kv_fmt="fp8", seed=21 + partition_size)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, partition_size=partition_size)
+    compare(got, ref, TOL_FP8, what=f"fp8 P{partition_size}")
+
+
+def test_fp8_every_code_decodes_exactly():
+    """Single cached token: out = v_scale * E4M3(code), every one of the 256 codes."""
+    _announce("fp8 all codes")
+    w = _small([1], kv_fmt="fp8", hq=2, hkv=2, seed=5, poison=False, extra_blocks=0)
+    codes = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    w.v_pool[0, :, 0, :] = codes
+    w.v_scale = np.ones(2, dtype=np.float32)
+    got = run_decode(w, out_dtype="f32")[0]
+    exp = oracle.e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(exp))
+    ok = ~np.isnan(exp)
+    np.testing.assert_array_equal(got[ok], exp[ok])
+
+
+def test_single_token_returns_its_value_exactly():
+    _announce("single token")
+    w = _small([1, 1, 1], seed=6)
+    got = run_decode(w, out_dtype="f32")
+    ref = oracle.paged_attention_workload(w)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_constant_v_is_exact():
+    _announce("constant V")
+    w = _small([1, 40, 1000, 3000], seed=7)
+    w.v_pool[...] = np.uint16(0x4000)       # 2.0
+    pa_inputs.poison_pool(w)
+    for P in (0, 128):
+        got = run_decode(w, out_dtype="f32", partition_size=P)
+        np.testing.assert_array_equal(got, 2.0)
+
+
+def test_one_hot_probes_bit_exact():
+    """One key scores 2^8 above all others: the output is exactly that token's V.
+
+    V holds small integers (exact in bf16) that encode (physical block, slot),
+    so a wrong gather shows up as a wrong integer.  t* sweeps the first and
+    last slot of every block and the last token.
+    """
+    _announce("one-hot probes")
+    bs = 16
+    L = 200
+    w = _small([L], bs=bs, hq=4, hkv=1, seed=8)
+    nblk = (L + bs - 1) // bs
+    # V[phys][0][slot][:] = phys * 16 + slot: integers < 256, exact in bf16
+    assert w.num_blocks <= 16
+    for j in range(nblk):
+        phys = w.block_table[0, j]
+        for sl in range(bs):
+            val = np.float32(phys * 16 + sl)
+            w.v_pool[phys, 0, sl, :] = pa_inputs.to_bf16_bits(np.full(128, val, np.float32))
+    q = np.zeros((1, 4, 128), np.float32)
+    q[0, :, 0] = 1.0
+    w.q = pa_inputs.to_bf16_bits(q)
+    targets = sorted({t for j in range(nblk) for t in (j * bs, min(j * bs + bs - 1, L - 1))} | {L - 1})
+    for tstar in targets:
+        w.k_pool[...] = 0
+        phys = w.block_table[0, tstar // bs]
+        # score gap: 1024 * scale * log2(e) ~ 130 (log2 units): others underflow to 0
+        w.k_pool[phys, 0, tstar % bs, 0] = pa_inputs.to_bf16_bits(np.array([1024.0], np.float32))[0]
+        pa_inputs.poison_pool(w)
+        got = run_decode(w, out_dtype="f32", partition_size=128)
+        exp = float(phys * 16 + tstar % bs)
+        assert np.all(got[0] == exp), (tstar, got[0, 0, :4], exp)
+
+
+def test_uniform_probe_mean():
+    """q = 0: every visible token gets the same weight; the output is the mean of V."""
+    _announce("q=0 mean")
+    w = _small([1, 17, 640, 1500], seed=9)
+    w.q[...] = 0
+    got = run_decode(w, out_dtype="f32")
+    ref = oracle.paged_attention_workload(w)
+    compare(got, ref, 1e-5, rel_tol=1e-4, what="mean")
+
+
+def test_block_permutation_bit_identical():
+    _announce("block permutation")
+    w = _small([33, 700, 1500, 16], seed=10)
+    a = run_decode(w, out_dtype="f32")
+    rng = np.random.default_rng(99)
+    perm = rng.permutation(w.num_blocks)
+    inv = np.argsort(perm)
+    w.k_pool = np.ascontiguousarray(w.k_pool[inv])
+    w.v_pool = np.ascontiguousarray(w.v_pool[inv])
+    w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    b = run_decode(w, out_dtype="f32")
+    np.testing.assert_array_equal(a, b)
+
+
+def test_partition_size_invariance():
+    _announce("partition invariance")
+    w = _small([50, 1000, 2500, 4096], seed=12)
+    outs = [run_decode(w, out_dtype="f32", partition_size=P) for P in (128, 256, 1024, 0)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-3
+
+
+def test_stages_equal_one_call():
+    """pa_decode_partials followed by pa_merge_partials equals pa_decode."""
+    _announce("stages")
+    import torch
+    from paged_kv_attention_13_amd import binding
+    from paged_kv_attention_13_amd.device import to_device
+    w = _small([300, 1200, 64], seed=13)
+    d = to_device(w)
+    out1 = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out1)
+    a = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                 w.scale, max_seq_len=w.max_seq_len, out=out1, partition_size=256)
+    pl = binding.plan(a)
+    assert pl.num_partitions == 5 and pl.workspace_bytes > 0
+    ws = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), pl.workspace_bytes
+    binding.decode_partials(a)
+    binding.merge_partials(a)
+    a.out = out2.data_ptr()
+    binding.decode_args_call(a)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+
+
+def test_empty_batch_is_a_no_op():
+    _announce("empty batch")
+    import torch
+    from paged_kv_attention_13_amd import binding
+    q = torch.zeros((0, 32, 128), dtype=torch.bfloat16, device="cuda")
+    kp = torch.zeros((1, 8, 16, 128), dtype=torch.bfloat16, device="cuda")
+    bt = torch.zeros((0, 1), dtype=torch.int32, device="cuda")
+    sl = torch.zeros((0,), dtype=torch.int32, device="cuda")
+    out = binding.decode(q, kp, kp, bt, sl, 0.1, max_seq_len=1)
+    assert out.shape == (0, 32, 128)
+
+
+# ----------------------------------------------------------------------------
+# the named workloads at full size (sampled rows against the oracle)
+# ----------------------------------------------------------------------------
+
+def _sampled_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(w.num_seqs, size=min(n, w.num_seqs), replace=False).tolist())
+    rows |= {int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens))}
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_named_workload_full_size(i):
+    _announce(f"workload {i}: {pa_inputs.WORKLOAD_NAMES[i]}")
+    w = pa_inputs.make_config(i)
+    got = run_decode(w)
+    rows = _sampled_rows(w, {1: 1, 2: 32, 3: 4, 4: 16}[i], seed=i)
+    ref = oracle.paged_attention_workload(w, rows=rows)
+    tol = {1: TOL_F32, 2: TOL_BF16, 3: TOL_BF16, 4: TOL_FP8}[i]
+    compare(got[rows], ref[rows], tol, what=f"workload {i} rows {rows[:6]}...")
+    # every row (not only the sampled ones) is finite
+    assert np.all(np.isfinite(got))
