@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the timed loop, run one device-to-device copy of this many MiB "
+                         "(a plain copy kernel of known size, to calibrate HBM byte counters)")
     return ap.parse_args()
 
 
@@ -146,6 +149,15 @@ def main():
             stages[1]()
             if evs:
                 evs[2].record()
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         run_step()

@@ -126,7 +126,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   const int end = min(part_start + p.partition_size, L);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index is uniform across the wave: keep it (and all tile/page arithmetic) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 7;                  // element slot inside the token row
   const int grp = lane >> 3;               // token group 0..7
   const int bs = p.block_size;
@@ -186,12 +187,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
       const int tok0 = part_start + t * TILE + 8 * r;
       const int page = min(tok0 >> log2bs, last_page);
       const int phys = __builtin_amdgcn_readlane(tbl, page - first_page);
-      const int slot = (tok0 + grp) & (bs - 1);
-      const size_t off = (size_t)phys * phys_stride + (size_t)slot * (D * EB) + lane_off;
+      // scalar page base + 32-bit per-lane offset (global_load ... saddr form)
+      const char *kp = kpool + (size_t)phys * phys_stride;
+      const char *vp = vpool + (size_t)phys * phys_stride;
+      const uint32_t off = (uint32_t)(((tok0 + grp) & (bs - 1)) * (D * EB) + lane_off);
 #pragma unroll
       for (int j = 0; j < EB; ++j) {
-        k[r][j] = *reinterpret_cast<const u32x4 *>(kpool + off + j * 128);
-        v[r][j] = *reinterpret_cast<const u32x4 *>(vpool + off + j * 128);
+        k[r][j] = *reinterpret_cast<const u32x4 *>(kp + off + j * 128);
+        v[r][j] = *reinterpret_cast<const u32x4 *>(vp + off + j * 128);
       }
     }
   };
@@ -351,22 +354,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
     }
   };
 
-  // software pipeline: the next tile's loads are in flight while this one is computed
-  int t = wave;
-  if (t < ntiles) {
-    load_tile(t, kr, vr);
-    for (; t < ntiles; t += NW) {
-      const int tn = (t + NW < ntiles) ? t + NW : t;
-      u32x4 kn[TPL][EB], vn[TPL][EB];
-      load_tile(tn, kn, vn);
+  // Double-buffered software pipeline over this wave's tiles t = wave, wave+NW, ...:
+  // two register sets, loads for one in flight while the other is computed.  Tile
+  // indices past the wave's last tile are clamped to it (an L2-resident reload), so
+  // every iteration issues the same loads and the wait counts stay static.
+  if (wave < ntiles) {
+    const int last = wave + ((ntiles - 1 - wave) / NW) * NW;   // this wave's last tile
+    u32x4 kb[TPL][EB], vb[TPL][EB];
+    load_tile(wave, kr, vr);
+    for (int t = wave; t <= last; t += 2 * NW) {
+      const int t1 = min(t + NW, last);
+      const int t2 = min(t + 2 * NW, last);
+      load_tile(t1, kb, vb);
       compute_tile(t, kr, vr);
-#pragma unroll
-      for (int r = 0; r < TPL; ++r)
-#pragma unroll
-        for (int j = 0; j < EB; ++j) {
-          kr[r][j] = kn[r][j];
-          vr[r][j] = vn[r][j];
-        }
+      load_tile(t2, kr, vr);
+      if (t + NW <= last) compute_tile(t + NW, kb, vb);
     }
   }
 

@@ -1,0 +1,90 @@
+"""GPU parity of pa_mixed (decode rows + causal prefill-chunk rows) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import pa_inputs
+from gpu_util import TOL_BF16, compare, run_mixed
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _mixed(dec_lens, pre, bs=16, hq=32, hkv=8, seed=0, poison=True):
+    """dec_lens: decode-row lengths; pre: list of (prior, q_len) prefill rows."""
+    L = list(dec_lens) + [p + n for p, n in pre]
+    ql = [1] * len(dec_lens) + [n for _, n in pre]
+    return pa_inputs.make_workload(name="mixed", seq_lens=L, q_lens=ql, num_q_heads=hq, num_kv_heads=hkv,
+                                   head_dim=128, block_size=bs, seed=seed, extra_blocks=3,
+                                   poison_unused=poison)
+
+
+PRE = [(0, 1), (0, 5), (0, 64), (3, 29), (17, 33), (100, 64), (250, 130), (0, 256), (1000, 96)]
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_mixed_ragged(bs):
+    _announce(f"mixed ragged bs={bs}")
+    w = _mixed([1, 40, 700, 3000], PRE, bs=bs, seed=bs)
+    ref = oracle.paged_attention_workload(w)
+    got = run_mixed(w)
+    compare(got, ref, TOL_BF16, what=f"mixed bs{bs}")
+
+
+def test_prefill_only_f32_out():
+    _announce("prefill only, f32 out")
+    w = _mixed([], PRE, seed=3)
+    ref = oracle.paged_attention_workload(w)
+    got = run_mixed(w, out_dtype="f32")
+    compare(got, ref, 1e-2, what="prefill f32 out")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8)])
+def test_prefill_group_sizes(hq, hkv):
+    _announce(f"prefill group hq={hq} hkv={hkv}")
+    w = _mixed([33], [(0, 40), (70, 100), (5, 200)], hq=hq, hkv=hkv, seed=hq)
+    ref = oracle.paged_attention_workload(w)
+    got = run_mixed(w, out_dtype="f32")
+    compare(got, ref, 1e-2, what=f"prefill G={hq // hkv}")
+
+
+def test_decode_row_equals_last_prefill_query():
+    """The last query of a prefill row and a decode row over the same cache agree."""
+    _announce("decode vs last prefill query")
+    w = _mixed([300], [(299 - 63, 64)], seed=5, poison=False)
+    w.block_table[1] = w.block_table[0]          # same cache, L = 300 for both rows
+    w.q[0] = w.q[1 + 63]                         # same query vector
+    got = run_mixed(w, out_dtype="f32")
+    assert np.max(np.abs(got[0] - got[64])) <= 5e-3
+
+
+def test_single_token_prefill_is_its_value():
+    _announce("prefill of one token from scratch")
+    w = _mixed([], [(0, 1), (0, 1)], seed=6)
+    got = run_mixed(w, out_dtype="f32")
+    ref = oracle.paged_attention_workload(w)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_prefill_constant_v_exact():
+    _announce("prefill constant V")
+    w = _mixed([9], [(0, 70), (130, 64)], seed=7)
+    w.v_pool[...] = np.uint16(0x4000)
+    pa_inputs.poison_pool(w)
+    got = run_mixed(w, out_dtype="f32")
+    np.testing.assert_array_equal(got, 2.0)
+
+
+def test_mixed_full_size_workload():
+    _announce(f"workload 5: {pa_inputs.WORKLOAD_NAMES[5]}")
+    w = pa_inputs.make_config(5)
+    got = run_mixed(w)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(5)
+    rows = sorted(set(rng.choice(96, size=6, replace=False).tolist()) | {96, 99, 103})
+    ref = oracle.paged_attention_workload(w, rows=rows)
+    idx = np.concatenate([np.arange(w.q_start_loc[b], w.q_start_loc[b + 1]) for b in rows])
+    compare(got[idx], ref[idx], TOL_BF16, what=f"workload 5 rows {rows}")
