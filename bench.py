@@ -37,13 +37,35 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
                     help="named workload (3 = 55 x 8192 bf16 decode, the headline)")
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--num-workers", type=int, default=0,
+                    help="decode work split into this many waves (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed loop, run one device-to-device copy of this many MiB "
                          "(a plain copy kernel of known size, to calibrate HBM byte counters)")
     return ap.parse_args()
+
+
+def committed_traffic(kv_fmt: str, workload_name: str):
+    """HBM bytes per launch of the decode kernel from the committed counter summary.
+
+    Returns None unless the summary covers this workload and the kernel source is
+    unchanged since the counters were taken (hash of decode.hip + pa_internal.h).
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_bf16_55x8192_bs64.md")
+    try:
+        text = open(path).read()
+        block = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in ("decode.hip", "pa_internal.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_attention_13_amd", "csrc", f), "rb").read())
+    if block.get("source_sha256_16") != h.hexdigest()[:16] or block.get("workload") != workload_name:
+        return None
+    return int(block["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, gpu_out, budget_s):
@@ -111,13 +133,13 @@ def main():
         m = binding.make_mixed_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
                                     d["q_start_loc"], w.scale, num_decode_rows=n_dec,
                                     max_q_len=int(w.q_lens[n_dec:].max()), max_seq_len=w.max_seq_len,
-                                    out=out, partition_size=args.partition_size)
+                                    out=out, num_workers=args.num_workers)
         nbytes = binding.mixed_workspace_bytes(m)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
         m.base.workspace, m.base.workspace_bytes = ws.data_ptr(), ws.numel()
         dec = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
                                        w.scale, max_seq_len=w.max_seq_len, out=out,
-                                       partition_size=args.partition_size)
+                                       num_workers=args.num_workers)
         dec.num_seqs = n_dec
         pl = binding.plan(dec)
         step = lambda: binding.mixed_args_call(m)  # noqa: E731
@@ -125,7 +147,7 @@ def main():
     else:
         a = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
                                      w.scale, max_seq_len=w.max_seq_len, k_scale=d["k_scale"],
-                                     v_scale=d["v_scale"], out=out, partition_size=args.partition_size)
+                                     v_scale=d["v_scale"], out=out, num_workers=args.num_workers)
         pl = binding.plan(a)
         ws = torch.empty(max(pl.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
         a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
@@ -183,8 +205,9 @@ def main():
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = split_bytes / (kernel_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "decode_kernel (split-K partials)" if not mixed else "pa_mixed call (all kernels)",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if mixed else committed_traffic(w.kv_fmt, w.name),
+                "kernel": "decode_kernel (balanced split, partials)" if not mixed else "pa_mixed call (all kernels)",
                 "kernel_ms_mean": round(kernel_ms, 5), "kernel_ms_p10": round(float(np.percentile(k_ms, 10)), 5),
                 "kernel_ms_p90": round(float(np.percentile(k_ms, 90)), 5),
                 "merge_ms_mean": round(float(np.mean(m_ms)), 5),
@@ -208,7 +231,7 @@ def main():
                    "context_tokens": int(w.seq_lens.sum()), "max_context": w.max_seq_len,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "kv_dtype": w.kv_fmt,
-                   "partition_size": pl.partition_size, "num_partitions": pl.num_partitions},
+                   "decode_workers": pl.num_workers, "tile_tokens": pl.tile_tokens},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_per_step * 1e-3), 1),

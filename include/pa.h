@@ -99,8 +99,9 @@ typedef struct pa_decode_args {
   int32_t num_blocks;          /* physical blocks in each pool */
   int32_t max_blocks_per_seq;  /* row stride of block_table */
   int32_t max_seq_len;         /* host-known upper bound on seq_lens (grid planning) */
-  int32_t partition_size;      /* split-K partition in tokens (multiple of 128, at most
-                                  64 * bs); 0 = the library chooses */
+  int32_t num_workers;         /* decode work split: the flattened (row, kv head, tile)
+                                  work is cut into this many equal ranges, one per
+                                  wave (1 .. 65536); 0 = the library chooses */
   int32_t q_dtype;             /* pa_dtype */
   int32_t kv_dtype;            /* pa_dtype */
   int32_t out_dtype;           /* pa_dtype */
@@ -113,7 +114,7 @@ typedef struct pa_decode_args {
   const int32_t *seq_lens;     /* [B], tokens in cache including the new one, >= 1 */
   float scale;                 /* softmax scale (1/sqrt(D) for standard attention) */
   void *out;                   /* [B][Hq][D], out_dtype */
-  void *workspace;             /* split-K partials; may be NULL when the plan needs 0 bytes */
+  void *workspace;             /* split records and partials (pa_decode_plan); NULL only when B == 0 */
   size_t workspace_bytes;
 } pa_decode_args;
 
@@ -131,33 +132,38 @@ typedef struct pa_mixed_args {
 
 /* Launch plan of a decode call. */
 typedef struct pa_plan {
-  int32_t partition_size;      /* tokens per split-K partition */
-  int32_t num_partitions;      /* partitions per row (from max_seq_len) */
-  size_t workspace_bytes;      /* 0 when num_partitions == 1 */
+  int32_t num_workers;         /* worker waves the decode kernel runs */
+  int32_t tile_tokens;         /* tokens per tile: 16 (f32, bf16 KV) or 32 (FP8 KV) */
+  size_t workspace_bytes;      /* per-unit split records + partial slots */
 } pa_plan;
 
 int pa_abi_version(void);
 
-/* Validate host-visible arguments and compute the split-K plan.  The plan is
- * a pure function of (num_seqs, Hq, Hkv, block_size, max_seq_len,
- * partition_size) and the device's compute-unit count. */
+/* Validate host-visible arguments and compute the decode plan.  The plan is a
+ * pure function of (num_seqs, Hq, Hkv, kv_dtype, max_seq_len, num_workers):
+ * it never reads device memory and never synchronises.  The workspace holds,
+ * for every (row, kv head) unit, the first worker covering it and their count
+ * (2 x int32), then (units + workers) partial slots of Hq/Hkv x (128 + 2) fp32. */
 pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
 
 /* Workspace bytes a pa_mixed call needs (its decode rows' split-K partials). */
 pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes);
 
-/* Decode attention over the paged cache: split-K partial kernel followed, when
- * the plan has more than one partition, by the log-sum-exp merge kernel.  Both
- * are queued on `stream`. */
+/* Decode attention over the paged cache: the decode kernel followed by the
+ * log-sum-exp merge kernel, both queued on `stream`.  The decode kernel cuts
+ * the flattened (row, kv head, tile) work into num_workers equal contiguous
+ * ranges (the split over the context that the dileepadev page names
+ * Flash-Decoding, section "Core Optimization Technologies"). */
 pa_status pa_decode(const pa_decode_args *a, void *stream);
 
-/* The two stages of pa_decode, callable separately (e.g. to time one, or to
- * merge partials gathered from elsewhere).  pa_decode_partials writes, for
- * every (row, q head, partition), the partition's running max m (log2
- * domain), its sum l of exp2(s - m) and the unnormalised sum of exp2(s - m) V
- * into the workspace; pa_merge_partials combines them into `out`.  With a
- * one-partition plan pa_decode_partials writes `out` directly and
- * pa_merge_partials does nothing. */
+/* The two stages of pa_decode, callable separately (e.g. to time one).
+ * pa_decode_partials writes `out` for every (row, kv head) unit that one
+ * worker covers whole; for a unit cut by worker boundaries it writes, per
+ * piece and query head, the running max m (log2 domain), the sum l of
+ * exp2(s - m) and the unnormalised sum of exp2(s - m) V into the workspace,
+ * plus the unit's (first worker, count) record.  pa_merge_partials combines
+ * the pieces of every cut unit into `out` and leaves the other rows alone.
+ * The merge must run after the partials call on the same workspace. */
 pa_status pa_decode_partials(const pa_decode_args *a, void *stream);
 pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
 

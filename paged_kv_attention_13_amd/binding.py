@@ -35,7 +35,7 @@ class DecodeArgs(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("max_blocks_per_seq", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int32),
-        ("partition_size", ctypes.c_int32),
+        ("num_workers", ctypes.c_int32),
         ("q_dtype", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
@@ -64,7 +64,7 @@ class MixedArgs(ctypes.Structure):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("partition_size", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
+    _fields_ = [("num_workers", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -142,7 +142,7 @@ def _stream(stream) -> int:
 
 
 def make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq_len: int,
-                     k_scale=None, v_scale=None, out=None, partition_size: int = 0,
+                     k_scale=None, v_scale=None, out=None, num_workers: int = 0,
                      workspace=None) -> DecodeArgs:
     a = DecodeArgs()
     a.num_seqs = int(seq_lens.shape[0])
@@ -153,7 +153,7 @@ def make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq
     a.num_blocks = int(k_pool.shape[0])
     a.max_blocks_per_seq = int(block_table.shape[1])
     a.max_seq_len = int(max_seq_len)
-    a.partition_size = int(partition_size)
+    a.num_workers = int(num_workers)
     a.q_dtype = dtype_code(q)
     a.kv_dtype = dtype_code(k_pool)
     a.out_dtype = dtype_code(out) if out is not None else a.q_dtype
@@ -191,13 +191,13 @@ def _alloc_workspace(nbytes: int, device):
 
 
 def decode(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq_len: int,
-           k_scale=None, v_scale=None, out=None, out_dtype=None, partition_size: int = 0,
+           k_scale=None, v_scale=None, out=None, out_dtype=None, num_workers: int = 0,
            workspace=None, stream=None):
     """Decode attention (``pa_decode``).  Returns ``out`` [B, Hq, D]."""
     if out is None:
         out = _alloc_out(q, out_dtype)
     a = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
-                         k_scale=k_scale, v_scale=v_scale, out=out, partition_size=partition_size)
+                         k_scale=k_scale, v_scale=v_scale, out=out, num_workers=num_workers)
     if workspace is None:
         workspace = _alloc_workspace(plan(a).workspace_bytes, q.device)
     if workspace is not None:
@@ -221,10 +221,10 @@ def decode_args_call(args: DecodeArgs, stream=None) -> None:
 
 def make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *,
                     num_decode_rows: int, max_q_len: int, max_seq_len: int, out=None,
-                    partition_size: int = 0) -> MixedArgs:
+                    num_workers: int = 0) -> MixedArgs:
     m = MixedArgs()
     m.base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
-                              out=out, partition_size=partition_size)
+                              out=out, num_workers=num_workers)
     m.q_start_loc = _ptr(q_start_loc)
     m.total_q = int(q.shape[0])
     m.num_decode_rows = int(num_decode_rows)
@@ -239,14 +239,14 @@ def mixed_workspace_bytes(m: MixedArgs) -> int:
 
 
 def mixed(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *, num_decode_rows: int,
-          max_q_len: int, max_seq_len: int, out=None, out_dtype=None, partition_size: int = 0,
+          max_q_len: int, max_seq_len: int, out=None, out_dtype=None, num_workers: int = 0,
           workspace=None, stream=None):
     """Mixed decode + chunked-prefill batch (``pa_mixed``).  Returns ``out`` [total_q, Hq, D]."""
     if out is None:
         out = _alloc_out(q, out_dtype)
     m = make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale,
                         num_decode_rows=num_decode_rows, max_q_len=max_q_len,
-                        max_seq_len=max_seq_len, out=out, partition_size=partition_size)
+                        max_seq_len=max_seq_len, out=out, num_workers=num_workers)
     if workspace is None:
         workspace = _alloc_workspace(mixed_workspace_bytes(m), q.device)
     if workspace is not None:

@@ -11,13 +11,21 @@
 // "Introduction to TensorRT-LLM" (dileepadev.github.io), section "Core
 // Optimization Technologies".
 //
-// Work decomposition.  One workgroup (4 x wave64) owns one (row b, kv head g,
-// partition s) unit: tokens [s*P, min((s+1)*P, L)).  The four waves take
-// interleaved tiles of 16 tokens (32 for FP8).  Inside a wave, 8 lanes share
-// one token: each lane holds 16 of its 128 elements, loaded with 16-byte
-// loads so that one load instruction covers eight whole 128-byte lines of a
-// (block, head) page.  The group of Hq/Hkv query heads that shares kv head g
-// is processed together, so every K/V byte is read from HBM once per step.
+// Work decomposition.  The work is the flattened sequence of (row, kv head,
+// 16-token tile) units (32-token tiles for FP8), cut into equal contiguous
+// ranges, one per worker wave; the launch holds about as many waves as the
+// chip keeps resident, so there is no tail of late workgroups and no empty
+// workgroup for short rows.  Each wave streams its range on its own (no LDS,
+// no barriers).  A unit covered by one wave is finished and written
+// directly; a unit cut by a range boundary leaves one partial (m, l, acc) per
+// piece, which the merge kernel combines with the log-sum-exp identity --
+// the split over the context named Flash-Decoding on the dileepadev page.
+// Inside a wave, 8 lanes share one token: each lane holds 16 of its 128
+// elements, loaded with 16-byte loads so that one load instruction covers
+// eight whole 128-byte lines of a (block, head) page; three register sets
+// keep two tiles in flight while the third is computed.  The Hq/Hkv query
+// heads that share kv head g are processed together, so every K/V byte is
+// read from HBM once per step.
 //
 // Arithmetic.  Q.K uses v_dot2c_f32_bf16 (bf16 pairs, fp32 accumulate); the
 // 8 partial sums of a token are combined with three DPP adds (quad xor 1,
@@ -32,11 +40,6 @@
 // v_dot2c_f32_bf16 (P rounded to bf16, the softmax denominator summed from the
 // same rounded values).  Tokens past the row's end are excluded by select and
 // their V registers zeroed, so NaN in unused slots never reaches the result.
-//
-// Epilogue.  The 32 (wave, token-group) partial states of a workgroup are
-// merged with one DPP step and one LDS pass using the log-sum-exp identity;
-// one-partition plans write the normalised output directly, otherwise
-// (m, l, acc) partials go to the workspace for merge_kernel.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -105,6 +108,22 @@ __device__ __forceinline__ void store_out(void *out, size_t idx, float v) {
   }
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ long long readlane64(long long v, int k) {
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFLL), k);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), k);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
 template <int KV, int G, bool OUT_BF16>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   constexpr int EB = KvTraits<KV>::EB;
@@ -112,350 +131,425 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   constexpr int TILE = 8 * TPL;            // tokens per tile
   constexpr int DW = 4 * EB;               // dwords per token per lane
   constexpr bool kBf = KV != PA_F32;
-
-  __shared__ float s_acc[NW][4][G][D];
-  __shared__ float s_m[NW][4][G];
-  __shared__ float s_l[NW][4][G];
-
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int L = p.seq_lens[b];
-  const int part_start = s * p.partition_size;
-  if (part_start >= L) return;           // whole workgroup: empty partition
-  const int end = min(part_start + p.partition_size, L);
+  constexpr int NBUF = (KV == PA_F32 || G >= 8) ? 2 : 3;   // tiles held in registers
 
   const int lane = threadIdx.x & 63;
-  // wave index is uniform across the wave: keep it (and all tile/page arithmetic) scalar
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 7;                  // element slot inside the token row
-  const int grp = lane >> 3;               // token group 0..7
-  const int bs = p.block_size;
-  const int log2bs = __builtin_ctz(bs);
-  const int first_page = part_start >> log2bs;
-  const int last_page = (end - 1) >> log2bs;
-  const int npages = last_page - first_page + 1;   // <= 64 by plan
+  // the wave index is uniform across the wave: keep it (and all work arithmetic) scalar
+  const int worker = blockIdx.x * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nworkers = p.num_workers;
+  if (worker >= nworkers) return;
+  const int B = p.num_seqs;
   const int Hq = p.num_q_heads;
   const int Hkv = p.num_kv_heads;
+  const int c = lane & 7;                  // element slot inside the token row
+  const int grp = lane >> 3;               // token group 0..7
 
-  // block-table entries of this partition: lane i holds page first_page + i
-  const int32_t *trow = p.block_table + (size_t)b * p.max_blocks_per_seq;
-  const int tbl = trow[first_page + min(lane, npages - 1)];
+  // ---- this worker's share of the flattened (row, kv head, tile) space ----
+  long long W = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int r = base + lane;
+    const int n = r < B ? (p.seq_lens[r] + TILE - 1) / TILE : 0;
+    W += __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), 63);
+  }
+  W *= Hkv;
+  // Planned launches hold two waves per SIMD.  With long work per wave one wave per SIMD
+  // streams HBM a little better (fewer concurrent page streams), so a planned launch
+  // with >= 128 tiles per wave at half the workers uses only the first half: whole
+  // workgroups, one per CU, the rest exit at once.
+  int nwk = nworkers;
+  if (p.workers_auto && (nwk % (2 * NW * kTargetCUs)) == 0 && W >= 128LL * (nwk / 2)) nwk /= 2;
+  // never more workers than tiles, so that every worker's range is non-empty and the
+  // workers covering a unit are exactly the consecutive ones from its first to its last
+  const int nw = (int)min((long long)nwk, W);
+  if (worker >= nw) return;
+  const long long x0 = (long long)worker * W / nw;
+  const long long x1 = (long long)(worker + 1) * W / nw;
+  // worker covering flattened tile index x: the largest w with w*W/nw <= x
+  auto worker_of = [&](long long x) { return (int)(((x + 1) * nw - 1) / W); };
 
-  // query group of kv head g, in this lane's element order
-  uint32_t qb[G][8];
-  float qf[G][16];
-  if constexpr (kBf) {
-    const uint16_t *q = static_cast<const uint16_t *>(p.q) + ((size_t)b * Hq + g * G) * D;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        qb[hh][i] = *reinterpret_cast<const uint32_t *>(q + hh * D + elem_d<EB>(c, 2 * i));
-  } else {
-    const float *q = static_cast<const float *>(p.q) + ((size_t)b * Hq + g * G) * D;
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) qf[hh][e] = q[hh * D + elem_d<EB>(c, e)];
+  // locate x0: row b whose units span [rowstart, rowstart + Hkv * n_b)
+  int b = 0;
+  long long rowstart = 0;
+  {
+    long long before = 0;
+    for (int base = 0; base < B; base += 64) {
+      const int r = base + lane;
+      const int n = r < B ? (p.seq_lens[r] + TILE - 1) / TILE : 0;
+      const int incl = wave_inclusive_scan(n, lane);
+      const long long lo = before + (long long)(incl - n) * Hkv;
+      const long long hi = before + (long long)incl * Hkv;
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(x0 >= lo && x0 < hi && n > 0);
+      if (hit != 0) {
+        const int k = __builtin_ctzll(hit);
+        b = base + k;
+        rowstart = readlane64(lo, k);
+        break;
+      }
+      before += (long long)__builtin_amdgcn_readlane(incl, 63) * Hkv;
+    }
   }
 
-  float qk_scale = p.scale * kLog2e;
-  if constexpr (KV == PA_FP8_E4M3) qk_scale *= p.k_scale[g];
-
+  const int bs = p.block_size;
+  const int log2bs = __builtin_ctz(bs);
   const size_t page_bytes = (size_t)bs * D * EB;
-  const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
-  const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
   const size_t phys_stride = (size_t)Hkv * page_bytes;
   const int lane_off = c * 16;
 
-  float m[G], l[G], acc[G][16];
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    m[hh] = kNegBig;
-    l[hh] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[hh][e] = 0.f;
-  }
+  int L = p.seq_lens[b];
+  int nb = (L + TILE - 1) / TILE;
+  int g = (int)((x0 - rowstart) / nb);
+  int t0 = (int)((x0 - rowstart) % nb);
+  long long ustart = rowstart + (long long)g * nb;
+  long long x = x0;
 
-  const int ntiles = (end - part_start + TILE - 1) / TILE;
-
-  u32x4 kr[TPL][EB], vr[TPL][EB];
-  auto load_tile = [&](int t, u32x4 (&k)[TPL][EB], u32x4 (&v)[TPL][EB]) {
-#pragma unroll
-    for (int r = 0; r < TPL; ++r) {
-      const int tok0 = part_start + t * TILE + 8 * r;
-      const int page = min(tok0 >> log2bs, last_page);
-      const int phys = __builtin_amdgcn_readlane(tbl, page - first_page);
-      // scalar page base + 32-bit per-lane offset (global_load ... saddr form)
-      const char *kp = kpool + (size_t)phys * phys_stride;
-      const char *vp = vpool + (size_t)phys * phys_stride;
-      const uint32_t off = (uint32_t)(((tok0 + grp) & (bs - 1)) * (D * EB) + lane_off);
-#pragma unroll
-      for (int j = 0; j < EB; ++j) {
-        k[r][j] = *reinterpret_cast<const u32x4 *>(kp + off + j * 128);
-        v[r][j] = *reinterpret_cast<const u32x4 *>(vp + off + j * 128);
-      }
+  while (x < x1) {
+    const int cnt = (int)min((long long)(nb - t0), x1 - x);
+    const int u = b * Hkv + g;
+    if (t0 == 0 && lane == 0) {
+      p.seg_first[u] = worker;
+      p.seg_count[u] = worker_of(ustart + nb - 1) - worker + 1;
     }
-  };
+    const bool whole = t0 == 0 && cnt == nb;
+    const int tok_begin = t0 * TILE;
+    const int tok_end = min((t0 + cnt) * TILE, L);
+    const int first_page = tok_begin >> log2bs;
+    const int last_page = (tok_end - 1) >> log2bs;
 
-  auto compute_tile = [&](int t, const u32x4 (&k)[TPL][EB], u32x4 (&v)[TPL][EB]) {
-    const int tile_start = part_start + t * TILE;
-    float sc[TPL][G];
+    // block-table entries, one per lane, for a chunk of up to 64 pages
+    const int32_t *trow = p.block_table + (size_t)b * p.max_blocks_per_seq;
+    const int mb_last = p.max_blocks_per_seq - 1;
+    int chunk_base = first_page;
+    int tbl = 0;
+
+    // query group of kv head g, in this lane's element order
+    uint32_t qb[G][8];
+    float qf[G][16];
+    if constexpr (kBf) {
+      const uint16_t *q = static_cast<const uint16_t *>(p.q) + ((size_t)b * Hq + g * G) * D;
 #pragma unroll
-    for (int r = 0; r < TPL; ++r) {
-      uint32_t kd[DW];
+      for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-      for (int i = 0; i < DW; ++i) kd[i] = k[r][i / 4][i % 4];
-      if constexpr (kBf) {
-        uint32_t kp[8];
-        if constexpr (KV == PA_BF16) {
+        for (int i = 0; i < 8; ++i)
+          qb[hh][i] = *reinterpret_cast<const uint32_t *>(q + hh * D + elem_d<EB>(c, 2 * i));
+    } else {
+      const float *q = static_cast<const float *>(p.q) + ((size_t)b * Hq + g * G) * D;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) kp[i] = kd[i];
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) qf[hh][e] = q[hh * D + elem_d<EB>(c, e)];
+    }
+    float qk_scale = p.scale * kLog2e;
+    if constexpr (KV == PA_FP8_E4M3) qk_scale *= p.k_scale[g];
+    const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
+    const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
+
+    float m[G], l[G], acc[G][16];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m[hh] = kNegBig;
+      l[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[hh][e] = 0.f;
+    }
+
+    auto load_tile = [&](int t, u32x4 (&k)[TPL][EB], u32x4 (&v)[TPL][EB]) {
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        const int tok0 = tok_begin + t * TILE + 8 * r;
+        const int page = min(tok0 >> log2bs, last_page);
+        const int phys = __builtin_amdgcn_readlane(tbl, page - chunk_base);
+        // scalar page base + 32-bit per-lane offset (global_load ... saddr form); the
+        // cache is streamed once per step, so the loads are non-temporal (measured
+        // ~10% more HBM bandwidth than cached loads on MI355X)
+        const char *kp = kpool + (size_t)phys * phys_stride;
+        const char *vp = vpool + (size_t)phys * phys_stride;
+        const uint32_t off = (uint32_t)(((tok0 + grp) & (bs - 1)) * (D * EB) + lane_off);
+#pragma unroll
+        for (int j = 0; j < EB; ++j) {
+          k[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + off + j * 128));
+          v[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + off + j * 128));
+        }
+      }
+    };
+
+    auto compute_tile = [&](int t, const u32x4 (&k)[TPL][EB], u32x4 (&v)[TPL][EB]) {
+      const int tile_start = tok_begin + t * TILE;
+      float sc[TPL][G];
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        uint32_t kd[DW];
+#pragma unroll
+        for (int i = 0; i < DW; ++i) kd[i] = k[r][i / 4][i % 4];
+        if constexpr (kBf) {
+          uint32_t kp[8];
+          if constexpr (KV == PA_BF16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kp[i] = kd[i];
+          } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              kp[2 * w] = fp8x2_to_bf16x2<false>(kd[w]);
+              kp[2 * w + 1] = fp8x2_to_bf16x2<true>(kd[w]);
+            }
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = dot2bf(qb[hh][i], kp[i], a);
+            sc[r][hh] = a;
+          }
         } else {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            kp[2 * w] = fp8x2_to_bf16x2<false>(kd[w]);
-            kp[2 * w + 1] = fp8x2_to_bf16x2<true>(kd[w]);
+          for (int hh = 0; hh < G; ++hh) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) a = __builtin_fmaf(qf[hh][e], __builtin_bit_cast(float, kd[e]), a);
+            sc[r][hh] = a;
           }
         }
+      }
+      // sum the 8 partial dot products of each token
+#pragma unroll
+      for (int r = 0; r < TPL; ++r)
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          float a = 0.f;
+          float y = sc[r][hh];
+          y += dpp<kDppXor1>(y);
+          y += dpp<kDppXor2>(y);
+          y += dpp<kDppHalfMirror>(y);
+          sc[r][hh] = y * qk_scale;
+        }
+      // tokens at or past the segment end take no part
+      if (tile_start + TILE > tok_end) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a = dot2bf(qb[hh][i], kp[i], a);
-          sc[r][hh] = a;
+        for (int r = 0; r < TPL; ++r) {
+          if (tile_start + 8 * r + grp >= tok_end) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) sc[r][hh] = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < EB; ++j) v[r][j] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+      // online softmax with lazy rescaling
+      float tmax[G];
+      bool need = false;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float y = sc[0][hh];
+#pragma unroll
+        for (int r = 1; r < TPL; ++r) y = fmaxf(y, sc[r][hh]);
+        tmax[hh] = y;
+        need |= y > m[hh] + kSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float mn = fmaxf(m[hh], tmax[hh]);
+          const float a = fast_exp2(m[hh] - mn);
+          m[hh] = mn;
+          l[hh] *= a;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[hh][e] *= a;
+        }
+      }
+      float pr[TPL][G];
+#pragma unroll
+      for (int r = 0; r < TPL; ++r)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) pr[r][hh] = fast_exp2(sc[r][hh] - m[hh]);
+
+      // P.V
+      if constexpr (kBf) {
+        constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 pair (1, 1)
+#pragma unroll
+        for (int w2 = 0; w2 < TPL / 2; ++w2) {
+          const int r0 = 2 * w2, r1 = 2 * w2 + 1;
+          uint32_t pp[G];
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            pp[hh] = pack_bf16(pr[r0][hh], pr[r1][hh]);
+            l[hh] = dot2bf(pp[hh], kOnes, l[hh]);
+          }
+          if constexpr (KV == PA_BF16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const uint32_t A = v[r0][i / 4][i % 4];
+              const uint32_t Bv = v[r1][i / 4][i % 4];
+              const uint32_t lo = __builtin_amdgcn_perm(Bv, A, 0x05040100u);
+              const uint32_t hi = __builtin_amdgcn_perm(Bv, A, 0x07060302u);
+#pragma unroll
+              for (int hh = 0; hh < G; ++hh) {
+                acc[hh][2 * i] = dot2bf(lo, pp[hh], acc[hh][2 * i]);
+                acc[hh][2 * i + 1] = dot2bf(hi, pp[hh], acc[hh][2 * i + 1]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t A = v[r0][0][w];
+              const uint32_t Bv = v[r1][0][w];
+              const uint32_t X = __builtin_amdgcn_perm(Bv, A, 0x05010400u);   // a0 b0 a1 b1
+              const uint32_t Y = __builtin_amdgcn_perm(Bv, A, 0x07030602u);   // a2 b2 a3 b3
+              const uint32_t v0 = fp8x2_to_bf16x2<false>(X);
+              const uint32_t v1 = fp8x2_to_bf16x2<true>(X);
+              const uint32_t v2 = fp8x2_to_bf16x2<false>(Y);
+              const uint32_t v3 = fp8x2_to_bf16x2<true>(Y);
+#pragma unroll
+              for (int hh = 0; hh < G; ++hh) {
+                acc[hh][4 * w + 0] = dot2bf(v0, pp[hh], acc[hh][4 * w + 0]);
+                acc[hh][4 * w + 1] = dot2bf(v1, pp[hh], acc[hh][4 * w + 1]);
+                acc[hh][4 * w + 2] = dot2bf(v2, pp[hh], acc[hh][4 * w + 2]);
+                acc[hh][4 * w + 3] = dot2bf(v3, pp[hh], acc[hh][4 * w + 3]);
+              }
+            }
+          }
         }
       } else {
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          float a = 0.f;
+        for (int r = 0; r < TPL; ++r) {
+          // copy out of the vector first: bit-casting a vector element in place is not
+          // reliable with this compiler (it reads element 0)
+          float vf[16];
 #pragma unroll
-          for (int e = 0; e < 16; ++e) a = __builtin_fmaf(qf[hh][e], __builtin_bit_cast(float, kd[e]), a);
-          sc[r][hh] = a;
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t bits = v[r][e / 4][e % 4];
+            vf[e] = __builtin_bit_cast(float, bits);
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            l[hh] += pr[r][hh];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[hh][e] = __builtin_fmaf(pr[r][hh], vf[e], acc[hh][e]);
+          }
         }
       }
-    }
-    // sum the 8 partial dot products of each token
-#pragma unroll
-    for (int r = 0; r < TPL; ++r)
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float x = sc[r][hh];
-        x += dpp<kDppXor1>(x);
-        x += dpp<kDppXor2>(x);
-        x += dpp<kDppHalfMirror>(x);
-        sc[r][hh] = x * qk_scale;
-      }
-    // tokens at or past `end` take no part
-    if (tile_start + TILE > end) {
-#pragma unroll
-      for (int r = 0; r < TPL; ++r) {
-        if (tile_start + 8 * r + grp >= end) {
-#pragma unroll
-          for (int hh = 0; hh < G; ++hh) sc[r][hh] = -__builtin_inff();
-#pragma unroll
-          for (int j = 0; j < EB; ++j) v[r][j] = u32x4{0u, 0u, 0u, 0u};
+    };
+
+    // Software pipeline over tiles [ta, tb) with NBUF register sets: while one tile
+    // is computed, the next NBUF-1 tiles are in flight.  Tile indices past the last
+    // are clamped to it (an L2-resident reload) so every step issues the same loads
+    // and the wait counts stay static.  Nothing else is loaded inside the pipeline:
+    // a conditional load there would make the compiler drain every load before each
+    // use of the block-table register.
+    auto run_tiles = [&](int ta, int tb) {
+      const int tl = tb - 1;
+      u32x4 ka[TPL][EB], va[TPL][EB], kb[TPL][EB], vb[TPL][EB];
+      load_tile(ta, ka, va);
+      if constexpr (NBUF == 3) {
+        u32x4 kc[TPL][EB], vc[TPL][EB];
+        load_tile(min(ta + 1, tl), kb, vb);
+        for (int t = ta; t < tb; t += 3) {
+          load_tile(min(t + 2, tl), kc, vc);
+          compute_tile(t, ka, va);
+          load_tile(min(t + 3, tl), ka, va);
+          if (t + 1 < tb) compute_tile(t + 1, kb, vb);
+          load_tile(min(t + 4, tl), kb, vb);
+          if (t + 2 < tb) compute_tile(t + 2, kc, vc);
+        }
+      } else {
+        for (int t = ta; t < tb; t += 2) {
+          load_tile(min(t + 1, tl), kb, vb);
+          compute_tile(t, ka, va);
+          load_tile(min(t + 2, tl), ka, va);
+          if (t + 1 < tb) compute_tile(t + 1, kb, vb);
         }
       }
+    };
+    // walk the segment in chunks of 64 pages (one block-table load per chunk); chunk
+    // boundaries fall on multiples of 64 pages, which are tile boundaries
+    for (int ta = 0; ta < cnt;) {
+      const int tb = min(cnt, (((chunk_base + 64) << log2bs) - tok_begin) / TILE);
+      tbl = trow[min(chunk_base + lane, mb_last)];
+      run_tiles(ta, tb);
+      ta = tb;
+      chunk_base += 64;
     }
-    // online softmax with lazy rescaling
-    float tmax[G];
-    bool need = false;
+
+    // ---- merge the 8 token groups of the wave (log-sum-exp), then store ----
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-      float x = sc[0][hh];
+      float M = m[hh];
+      M = fmaxf(M, dpp<kDppRowRor8>(M));
+      M = fmaxf(M, __shfl_xor(M, 16));
+      M = fmaxf(M, __shfl_xor(M, 32));
+      const float a = fast_exp2(m[hh] - M);
+      m[hh] = M;
+      float lv = l[hh] * a;
+      lv += dpp<kDppRowRor8>(lv);
+      lv += __shfl_xor(lv, 16);
+      lv += __shfl_xor(lv, 32);
+      l[hh] = lv;
 #pragma unroll
-      for (int r = 1; r < TPL; ++r) x = fmaxf(x, sc[r][hh]);
-      tmax[hh] = x;
-      need |= x > m[hh] + kSlack;
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        const float mn = fmaxf(m[hh], tmax[hh]);
-        const float a = fast_exp2(m[hh] - mn);
-        m[hh] = mn;
-        l[hh] *= a;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[hh][e] *= a;
+      for (int e = 0; e < 16; ++e) {
+        float y = acc[hh][e] * a;
+        y += dpp<kDppRowRor8>(y);
+        y += __shfl_xor(y, 16);
+        y += __shfl_xor(y, 32);
+        acc[hh][e] = y;
       }
     }
-    float pr[TPL][G];
+    float vscale = 1.f;
+    if constexpr (KV == PA_FP8_E4M3) vscale = p.v_scale[g];
+    // token group hh writes head hh (all 16 of its elements per lane)
 #pragma unroll
-    for (int r = 0; r < TPL; ++r)
+    for (int hh = 0; hh < G; ++hh) {
+      if (grp != hh) continue;
+      const int h = g * G + hh;
+      if (whole) {
+        const size_t base = ((size_t)b * Hq + h) * D;
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) pr[r][hh] = fast_exp2(sc[r][hh] - m[hh]);
-
-    // P.V
-    if constexpr (kBf) {
-      constexpr uint32_t kOnes = 0x3F803F80u;   // bf16 pair (1, 1)
+        for (int e = 0; e < 16; ++e)
+          store_out<OUT_BF16>(p.out, base + elem_d<EB>(c, e), acc[hh][e] * vscale / l[hh]);
+      } else {
+        const size_t slot = (size_t)(u + worker) * G + hh;
 #pragma unroll
-      for (int u = 0; u < TPL / 2; ++u) {
-        const int r0 = 2 * u, r1 = 2 * u + 1;
-        uint32_t pp[G];
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          pp[hh] = pack_bf16(pr[r0][hh], pr[r1][hh]);
-          l[hh] = dot2bf(pp[hh], kOnes, l[hh]);
-        }
-        if constexpr (KV == PA_BF16) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t A = v[r0][i / 4][i % 4];
-            const uint32_t B = v[r1][i / 4][i % 4];
-            const uint32_t lo = __builtin_amdgcn_perm(B, A, 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(B, A, 0x07060302u);
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-              acc[hh][2 * i] = dot2bf(lo, pp[hh], acc[hh][2 * i]);
-              acc[hh][2 * i + 1] = dot2bf(hi, pp[hh], acc[hh][2 * i + 1]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t A = v[r0][0][w];
-            const uint32_t B = v[r1][0][w];
-            const uint32_t X = __builtin_amdgcn_perm(B, A, 0x05010400u);   // a0 b0 a1 b1
-            const uint32_t Y = __builtin_amdgcn_perm(B, A, 0x07030602u);   // a2 b2 a3 b3
-            const uint32_t v0 = fp8x2_to_bf16x2<false>(X);
-            const uint32_t v1 = fp8x2_to_bf16x2<true>(X);
-            const uint32_t v2 = fp8x2_to_bf16x2<false>(Y);
-            const uint32_t v3 = fp8x2_to_bf16x2<true>(Y);
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-              acc[hh][4 * w + 0] = dot2bf(v0, pp[hh], acc[hh][4 * w + 0]);
-              acc[hh][4 * w + 1] = dot2bf(v1, pp[hh], acc[hh][4 * w + 1]);
-              acc[hh][4 * w + 2] = dot2bf(v2, pp[hh], acc[hh][4 * w + 2]);
-              acc[hh][4 * w + 3] = dot2bf(v3, pp[hh], acc[hh][4 * w + 3]);
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < TPL; ++r) {
-        // copy out of the vector first: bit-casting a vector element in place is not
-        // reliable with this compiler (it reads element 0)
-        float vf[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t bits = v[r][e / 4][e % 4];
-          vf[e] = __builtin_bit_cast(float, bits);
-        }
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          l[hh] += pr[r][hh];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[hh][e] = __builtin_fmaf(pr[r][hh], vf[e], acc[hh][e]);
+        for (int e = 0; e < 16; ++e) p.part_acc[slot * D + elem_d<EB>(c, e)] = acc[hh][e] * vscale;
+        if (c == 0) {
+          p.part_m[slot] = m[hh];
+          p.part_l[slot] = l[hh];
         }
       }
     }
-  };
 
-  // Double-buffered software pipeline over this wave's tiles t = wave, wave+NW, ...:
-  // two register sets, loads for one in flight while the other is computed.  Tile
-  // indices past the wave's last tile are clamped to it (an L2-resident reload), so
-  // every iteration issues the same loads and the wait counts stay static.
-  if (wave < ntiles) {
-    const int last = wave + ((ntiles - 1 - wave) / NW) * NW;   // this wave's last tile
-    u32x4 kb[TPL][EB], vb[TPL][EB];
-    load_tile(wave, kr, vr);
-    for (int t = wave; t <= last; t += 2 * NW) {
-      const int t1 = min(t + NW, last);
-      const int t2 = min(t + 2 * NW, last);
-      load_tile(t1, kb, vb);
-      compute_tile(t, kr, vr);
-      load_tile(t2, kr, vr);
-      if (t + NW <= last) compute_tile(t + NW, kb, vb);
-    }
-  }
-
-  // ---- epilogue: merge token groups k and k^1 of each 16-lane row (DPP) ----
-#pragma unroll
-  for (int hh = 0; hh < G; ++hh) {
-    const float mo = dpp<kDppRowRor8>(m[hh]);
-    const float mn = fmaxf(m[hh], mo);
-    const float a = fast_exp2(m[hh] - mn);
-    m[hh] = mn;
-    l[hh] *= a;
-    l[hh] += dpp<kDppRowRor8>(l[hh]);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      acc[hh][e] *= a;
-      acc[hh][e] += dpp<kDppRowRor8>(acc[hh][e]);
-    }
-  }
-  const int row16 = lane >> 4;
-  if ((lane & 8) == 0) {
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s_acc[wave][row16][hh][elem_d<EB>(c, e)] = acc[hh][e];
-    if (c == 0) {
-#pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        s_m[wave][row16][hh] = m[hh];
-        s_l[wave][row16][hh] = l[hh];
-      }
-    }
-  }
-  __syncthreads();
-
-  float vscale = 1.f;
-  if constexpr (KV == PA_FP8_E4M3) vscale = p.v_scale[g];
-  const int S = p.num_partitions;
-  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
-    const int hh = idx / D;
-    const int d = idx % D;
-    float M = kNegBig;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) M = fmaxf(M, s_m[w][k][hh]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float wt = fast_exp2(s_m[w][k][hh] - M);
-        num = __builtin_fmaf(wt, s_acc[w][k][hh][d], num);
-        den = __builtin_fmaf(wt, s_l[w][k][hh], den);
-      }
-    num *= vscale;
-    const int h = g * G + hh;
-    if (S == 1) {
-      store_out<OUT_BF16>(p.out, ((size_t)b * Hq + h) * D + d, num / den);
-    } else {
-      const size_t pi = ((size_t)b * Hq + h) * S + s;
-      p.part_acc[pi * D + d] = num;
-      if (d == 0) {
-        p.part_m[pi] = M;
-        p.part_l[pi] = den;
+    // next unit
+    x += cnt;
+    t0 = 0;
+    ustart += nb;
+    if (++g == Hkv) {
+      g = 0;
+      ++b;
+      if (x < x1) {
+        L = p.seq_lens[b];
+        nb = (L + TILE - 1) / TILE;
       }
     }
   }
 }
 
-// Combine the per-partition partials of one (row, query head): the
-// log-sum-exp identity  o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Combine the partials of one (row, query head) whose unit was split across
+// workers: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch p) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int L = p.seq_lens[b];
-  const int S = p.num_partitions;
-  const int Sb = (L + p.partition_size - 1) / p.partition_size;
-  const size_t base = ((size_t)b * p.num_q_heads + h) * S;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  const int g = h / G;
+  const int hh = h % G;
+  const int u = b * p.num_kv_heads + g;
+  const int cnt = p.seg_count[u];
+  if (cnt <= 1) return;                    // written directly by its only worker
+  const int first = p.seg_first[u];
   float M = kNegBig;
-  for (int s = 0; s < Sb; ++s) M = fmaxf(M, p.part_m[base + s]);
+  for (int i = 0; i < cnt; ++i) M = fmaxf(M, p.part_m[(size_t)(u + first + i) * G + hh]);
   float n0 = 0.f, n1 = 0.f, den = 0.f;
-  for (int s = 0; s < Sb; ++s) {
-    const float wt = fast_exp2(p.part_m[base + s] - M);
-    den = __builtin_fmaf(wt, p.part_l[base + s], den);
-    const float2 a = *reinterpret_cast<const float2 *>(p.part_acc + (base + s) * D + 2 * lane);
+  for (int i = 0; i < cnt; ++i) {
+    const size_t slot = (size_t)(u + first + i) * G + hh;
+    const float wt = fast_exp2(p.part_m[slot] - M);
+    den = __builtin_fmaf(wt, p.part_l[slot], den);
+    const float2 a = *reinterpret_cast<const float2 *>(p.part_acc + slot * D + 2 * lane);
     n0 = __builtin_fmaf(wt, a.x, n0);
     n1 = __builtin_fmaf(wt, a.y, n1);
   }
@@ -466,7 +560,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch p) {
 
 template <int KV, int G>
 int launch_kv_g(const DecodeLaunch &L, hipStream_t st) {
-  dim3 grid(L.num_partitions, L.num_kv_heads, L.num_seqs);
+  dim3 grid((L.num_workers + NW - 1) / NW);
   if (L.out_dtype == PA_BF16)
     hipLaunchKernelGGL((decode_kernel<KV, G, true>), grid, dim3(NT), 0, st, L);
   else

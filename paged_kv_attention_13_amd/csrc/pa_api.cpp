@@ -34,7 +34,7 @@ pa_status pa_merge_partials(const pa_decode_args *a, void *stream) {
   pa_plan plan;
   DecodeLaunch L;
   pa_status s = prepare_decode(a, &plan, &L);
-  if (s != PA_OK || a->num_seqs == 0 || plan.num_partitions <= 1) return s;
+  if (s != PA_OK || a->num_seqs == 0) return s;
   return hip_status(launch_merge(L, stream), "merge");
 }
 
@@ -44,7 +44,7 @@ pa_status pa_decode(const pa_decode_args *a, void *stream) {
   pa_status s = prepare_decode(a, &plan, &L);
   if (s != PA_OK || a->num_seqs == 0) return s;
   s = hip_status(launch_decode_partials(L, stream), "decode");
-  if (s != PA_OK || plan.num_partitions <= 1) return s;
+  if (s != PA_OK) return s;
   return hip_status(launch_merge(L, stream), "merge");
 }
 
@@ -103,7 +103,7 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
   }
   if (d.num_seqs > 0) {
     s = hip_status(launch_decode_partials(L, stream), "decode");
-    if (s != PA_OK || plan.num_partitions <= 1) return s;
+    if (s != PA_OK) return s;
     return hip_status(launch_merge(L, stream), "merge");
   }
   return PA_OK;

@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument validation, split-K planning, metadata
 // checks and error reporting.  Plain C++ (no HIP calls) so that it can be
 // built and tested on a machine without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -78,13 +79,8 @@ pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers) {
   const bool fp8 = a->kv_dtype == PA_FP8_E4M3;
   if (!fp8 && (a->k_scale || a->v_scale))
     return set_error(PA_ERR_BAD_DTYPE, "k_scale/v_scale are only used with an FP8 KV cache");
-  if (a->partition_size != 0) {
-    if (a->partition_size % kPartitionQuantum != 0 ||
-        a->partition_size > kMaxPagesPerPartition * a->block_size)
-      return set_error(PA_ERR_UNSUPPORTED,
-                       "partition_size=%d must be a multiple of %d and at most %d (64 blocks)",
-                       a->partition_size, kPartitionQuantum, kMaxPagesPerPartition * a->block_size);
-  }
+  if (a->num_workers < 0 || a->num_workers > 65536)
+    return set_error(PA_ERR_UNSUPPORTED, "num_workers=%d outside [0, 65536]", a->num_workers);
   if (need_device_pointers && a->num_seqs > 0) {
     if (!a->q || !a->k_pool || !a->v_pool || !a->block_table || !a->seq_lens || !a->out)
       return set_error(PA_ERR_NULL_POINTER, "q, k_pool, v_pool, block_table, seq_lens and out are required");
@@ -98,32 +94,27 @@ pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers) {
   return PA_OK;
 }
 
+int tile_tokens(int kv_dtype) { return kv_dtype == PA_FP8_E4M3 ? 32 : 16; }
+
 pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
-  const int bs = a->block_size;
-  const int max_p = kMaxPagesPerPartition * bs;
-  int P = a->partition_size;
-  if (P == 0) {
-    // Choose the largest partition that still yields enough workgroups to
-    // fill the chip: units = rows * kv heads; each unit is split into
-    // ceil(max_seq_len / P) partitions of 4 waves.
+  const int tile = tile_tokens(a->kv_dtype);
+  int nw = a->num_workers;
+  if (nw == 0) {
+    // about as many waves as the chip keeps resident, but at least a few tiles each
     const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
-    const int64_t target = 4LL * kTargetCUs;   // >= ~4 workgroups per CU
-    P = kPartitionQuantum;
-    for (int cand = max_p; cand >= kPartitionQuantum; cand /= 2) {
-      if (cand % kPartitionQuantum) continue;
-      const int64_t parts = (a->max_seq_len + cand - 1) / cand;
-      if (units * parts >= target || cand == kPartitionQuantum) { P = cand; break; }
-    }
+    const int64_t tiles_upper = units * ((a->max_seq_len + tile - 1) / tile);
+    nw = (int)std::min<int64_t>(kMaxWorkers, std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) /
+                                                                     kMinTilesPerWorker));
   }
-  const int S = a->max_seq_len > 0 ? (a->max_seq_len + P - 1) / P : 1;
-  plan->partition_size = P;
-  plan->num_partitions = S;
-  if (S <= 1 || a->num_seqs == 0) {
+  plan->num_workers = nw;
+  plan->tile_tokens = tile;
+  if (a->num_seqs == 0) {
     plan->workspace_bytes = 0;
   } else {
-    const size_t n = (size_t)a->num_seqs * a->num_q_heads * S;
-    plan->workspace_bytes = 2 * round_up(n * sizeof(float), 256) +
-                            round_up(n * kHeadDim * sizeof(float), 256);
+    const size_t units = (size_t)a->num_seqs * a->num_kv_heads;
+    const size_t slots = (units + nw) * (size_t)(a->num_q_heads / a->num_kv_heads);
+    plan->workspace_bytes = round_up(2 * units * sizeof(int32_t), 256) + 2 * round_up(slots * sizeof(float), 256) +
+                            round_up(slots * kHeadDim * sizeof(float), 256);
   }
   return PA_OK;
 }
@@ -143,20 +134,26 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   L->num_kv_heads = a->num_kv_heads;
   L->block_size = a->block_size;
   L->max_blocks_per_seq = a->max_blocks_per_seq;
-  L->partition_size = plan.partition_size;
-  L->num_partitions = plan.num_partitions;
+  L->num_workers = plan.num_workers;
+  L->workers_auto = a->num_workers == 0;
   L->kv_dtype = a->kv_dtype;
   L->out_dtype = a->out_dtype;
   L->scale = a->scale;
-  if (plan.workspace_bytes > 0) {
+  if (a->num_seqs > 0) {
     if (!a->workspace || a->workspace_bytes < plan.workspace_bytes)
       return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, plan needs %zu",
                        a->workspace ? a->workspace_bytes : (size_t)0, plan.workspace_bytes);
-    const size_t n = (size_t)a->num_seqs * a->num_q_heads * plan.num_partitions;
+    const size_t units = (size_t)a->num_seqs * a->num_kv_heads;
+    const size_t slots = (units + plan.num_workers) * (size_t)(a->num_q_heads / a->num_kv_heads);
     char *base = static_cast<char *>(a->workspace);
+    L->seg_first = reinterpret_cast<int32_t *>(base);
+    L->seg_count = L->seg_first + units;
+    base += round_up(2 * units * sizeof(int32_t), 256);
     L->part_m = reinterpret_cast<float *>(base);
-    L->part_l = reinterpret_cast<float *>(base + round_up(n * sizeof(float), 256));
-    L->part_acc = reinterpret_cast<float *>(base + 2 * round_up(n * sizeof(float), 256));
+    base += round_up(slots * sizeof(float), 256);
+    L->part_l = reinterpret_cast<float *>(base);
+    base += round_up(slots * sizeof(float), 256);
+    L->part_acc = reinterpret_cast<float *>(base);
   }
   return PA_OK;
 }

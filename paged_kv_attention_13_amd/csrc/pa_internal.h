@@ -12,10 +12,11 @@ namespace pa {
 
 // Shapes the kernels are compiled for.
 constexpr int kHeadDim = 128;
-constexpr int kWavesPerBlock = 4;        // decode kernel: 4 wave64 per workgroup
-constexpr int kPartitionQuantum = 128;   // partition sizes are multiples of this
-constexpr int kMaxPagesPerPartition = 64;  // one block-table entry per lane of a wave
+constexpr int kWavesPerBlock = 4;        // decode kernel: 4 independent wave64 workers per workgroup
 constexpr int kTargetCUs = 256;          // MI355X compute units (grid planning only)
+constexpr int kWorkersPerCU = 8;         // resident decode waves per CU (2 per SIMD)
+constexpr int kMaxWorkers = kTargetCUs * kWorkersPerCU;
+constexpr int kMinTilesPerWorker = 4;    // below this, fewer workers are launched
 
 // Everything a decode launch needs, resolved on the host.
 struct DecodeLaunch {
@@ -27,16 +28,18 @@ struct DecodeLaunch {
   const int32_t *block_table;
   const int32_t *seq_lens;
   void *out;
-  float *part_m;      // [B][Hq][S]
-  float *part_l;      // [B][Hq][S]
-  float *part_acc;    // [B][Hq][S][D]
+  int32_t *seg_first;  // [B*Hkv] first worker covering each (row, kv head) unit
+  int32_t *seg_count;  // [B*Hkv] number of workers covering it
+  float *part_m;       // [(B*Hkv + workers) * G]   partial slot (unit + worker), head in group
+  float *part_l;       // same
+  float *part_acc;     // [(B*Hkv + workers) * G][D]
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
   int block_size;
   int max_blocks_per_seq;
-  int partition_size;
-  int num_partitions;
+  int num_workers;
+  int workers_auto;    // 1 when the library chose num_workers (the kernel may use fewer)
   int kv_dtype;
   int out_dtype;
   float scale;
@@ -67,6 +70,7 @@ pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers);
 pa_status plan_decode(const pa_decode_args *a, pa_plan *plan);
 pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, DecodeLaunch *L);
 size_t elem_bytes(int dtype);
+int tile_tokens(int kv_dtype);
 
 // Kernel launchers (decode.hip, prefill.hip).  Return 0 on success, else the
 // HIP error code of the failed launch.

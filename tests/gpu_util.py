@@ -7,7 +7,7 @@ TOL_REL_L2 = 1e-2      # ||gpu - oracle||_2 / ||oracle||_2 (catches small system
 TOL_F32 = 1e-4         # fp32 path (fp32 in, fp32 out)
 
 
-def run_decode(w, out_dtype=None, partition_size=0, dev=None):
+def run_decode(w, out_dtype=None, num_workers=0, dev=None):
     import torch
     from paged_kv_attention_13_amd import binding
     from paged_kv_attention_13_amd.device import to_device
@@ -15,12 +15,12 @@ def run_decode(w, out_dtype=None, partition_size=0, dev=None):
     odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
     out = binding.decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], w.scale,
                          max_seq_len=w.max_seq_len, k_scale=d["k_scale"], v_scale=d["v_scale"],
-                         out_dtype=odt, partition_size=partition_size)
+                         out_dtype=odt, num_workers=num_workers)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 
 
-def run_mixed(w, out_dtype=None, partition_size=0, dev=None):
+def run_mixed(w, out_dtype=None, num_workers=0, dev=None):
     import torch
     from paged_kv_attention_13_amd import binding
     from paged_kv_attention_13_amd.device import to_device
@@ -30,7 +30,7 @@ def run_mixed(w, out_dtype=None, partition_size=0, dev=None):
     out = binding.mixed(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
                         d["q_start_loc"], w.scale, num_decode_rows=w.num_decode_rows,
                         max_q_len=int(prefill_q.max()) if len(prefill_q) else 1,
-                        max_seq_len=w.max_seq_len, out_dtype=odt, partition_size=partition_size)
+                        max_seq_len=w.max_seq_len, out_dtype=odt, num_workers=num_workers)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 

@@ -46,6 +46,7 @@ def test_abi_version(b):
 def test_struct_layout_matches_header(b):
     # field offsets of the C struct on x86-64 (12 int32, then pointers, float, ...)
     assert b.DecodeArgs.q.offset == 48
+    assert b.DecodeArgs.num_workers.offset == 32
     assert b.DecodeArgs.scale.offset == 48 + 7 * 8
     assert ctypes.sizeof(b.DecodeArgs) == 48 + 7 * 8 + 8 + 3 * 8
     assert b.MixedArgs.q_start_loc.offset == ctypes.sizeof(b.DecodeArgs)
@@ -81,8 +82,8 @@ BAD = [
     (dict(out=None), "PA_ERR_NULL_POINTER"),
     (dict(q=0x10008), "PA_ERR_MISALIGNED"),
     (dict(k_pool=0x10004), "PA_ERR_MISALIGNED"),
-    (dict(partition_size=100), "PA_ERR_UNSUPPORTED"),
-    (dict(partition_size=2048), "PA_ERR_UNSUPPORTED"),               # > 64 blocks of 16
+    (dict(num_workers=-1), "PA_ERR_UNSUPPORTED"),
+    (dict(num_workers=70000), "PA_ERR_UNSUPPORTED"),
     (dict(max_seq_len=1000, max_blocks_per_seq=64), "PA_ERR_WORKSPACE_TOO_SMALL"),
 ]
 
@@ -102,22 +103,27 @@ def test_null_struct(b):
 
 
 def test_plan_choices(b):
-    # long context: split so that ~4 workgroups per CU exist
+    # long context: about as many workers as the chip keeps resident
     a = _args(b, num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192)
     p = b.plan(a)
-    assert p.partition_size % 128 == 0 and p.partition_size <= 64 * 64
-    assert p.num_partitions == -(-8192 // p.partition_size)
-    assert 55 * 8 * p.num_partitions >= 1024
-    n = 55 * 32 * p.num_partitions
-    assert p.workspace_bytes >= n * (128 + 2) * 4
-    # explicit partition size is honoured
-    a.partition_size = 256
+    assert p.num_workers == 2048 and p.tile_tokens == 16
+    units = 55 * 8
+    slots = (units + 2048) * 4
+    assert p.workspace_bytes >= 2 * units * 4 + slots * (128 + 2) * 4
+    # FP8 KV uses 32-token tiles
+    a.kv_dtype = 2
+    a.k_scale = a.v_scale = 0x10000
+    assert b.plan(a).tile_tokens == 32
+    # an explicit worker count is honoured
+    a = _args(b, num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192, num_workers=7)
+    assert b.plan(a).num_workers == 7
+    # tiny work: fewer workers, at least a few tiles each
+    a = _args(b, num_seqs=1, max_seq_len=512, max_blocks_per_seq=32)
     p = b.plan(a)
-    assert (p.partition_size, p.num_partitions) == (256, 32)
-    # one partition: no workspace
-    a = _args(b, num_seqs=2000, max_seq_len=100)
-    p = b.plan(a)
-    assert p.num_partitions == 1 and p.workspace_bytes == 0
+    assert p.num_workers == 8 * 32 // 4
+    # no rows: no workspace
+    a = _args(b, num_seqs=0)
+    assert b.plan(a).workspace_bytes == 0
 
 
 def test_mixed_validation(b):
