@@ -14,9 +14,12 @@
 //
 // Tiling.  A workgroup (4 x wave64) owns one (row, kv head, block of query
 // heads, query tile); each wave owns 32 query positions of one query head.
-// K/V are staged through LDS in tiles of 64 tokens gathered page by page
-// through the block table; the next tile is prefetched into registers while
-// the current one is computed.  Per tile and wave:
+// K/V are staged through two LDS buffers in tiles of 64 tokens gathered page
+// by page through the block table: while tile j is computed, tile j+1 sits in
+// the other buffer and tile j+2's global loads are in flight; one barrier per
+// tile.  Each loading thread holds 4 consecutive tokens of 8 head-dim
+// elements, so V^T is formed in registers (byte permutes) and written with
+// 8-byte LDS stores.  Per tile and wave:
 //   S^T = K Q^T   : 32 x v_mfma_f32_16x16x32_bf16  (A = K rows from LDS,
 //                   B = Q^T held in registers for the whole row)
 //   online softmax in fp32 (log2 domain, lazy rescale as in the decode kernel)
@@ -55,6 +58,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kSlack = 8.0f;
 constexpr int CHUNKS = KT * D * 2 / 16 / NTP;   // 16-byte chunks per thread per tile (K or V): 4
+constexpr int kTblLds = 1024;      // block-table entries staged in LDS (longer ranges read global memory)
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -66,7 +70,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float bf16_round(float x) { return (float)(__bf16)x; }
+
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -82,12 +86,15 @@ __device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
 
 // HB: query heads per workgroup (1, 2 or 4); the 4 waves cover HB heads x (4/HB) query sub-tiles.
 template <int HB, bool OUT_BF16>
-__global__ __launch_bounds__(NTP) void prefill_kernel(PrefillLaunch p) {
+__global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_kernel(PrefillLaunch p) {
   constexpr int QSUB = NWP / HB;
   constexpr int QB = QW * QSUB;            // queries per workgroup
 
-  __shared__ __attribute__((aligned(16))) char s_k[KT * K_STRIDE];
-  __shared__ __attribute__((aligned(16))) char s_vt[D * V_STRIDE];
+  // two LDS buffers: tile j is computed from buffer j&1 while tile j+1 is stored to the other
+  __shared__ __attribute__((aligned(16))) char s_k[2][KT * K_STRIDE];
+  __shared__ __attribute__((aligned(16))) char s_vt[2][D * V_STRIDE];
+  __shared__ int s_tbl[kTblLds];           // block-table entries of the pages this workgroup visits
 
   const int Hq = p.num_q_heads;
   const int Hkv = p.num_kv_heads;
@@ -134,7 +141,8 @@ __global__ __launch_bounds__(NTP) void prefill_kernel(PrefillLaunch p) {
   }
   const float qk_scale = p.scale * kLog2e;
 
-  // cooperative tile loads: thread chunk c = tid + 256*i -> token c/16, elements 8*(c%16)..+8
+  // cooperative tile loads: thread -> 4 consecutive tokens 4*tq .. 4*tq+3, elements 8*dg .. 8*dg+7,
+  // so each load instruction of a wave covers four whole 256-byte token rows
   const int bs = p.block_size;
   const int log2bs = __builtin_ctz(bs);
   const int32_t *trow = p.block_table + (size_t)row * p.max_blocks_per_seq;
@@ -142,36 +150,54 @@ __global__ __launch_bounds__(NTP) void prefill_kernel(PrefillLaunch p) {
   const __bf16 *kpool = static_cast<const __bf16 *>(p.k_pool) + (size_t)g * page_elems;
   const __bf16 *vpool = static_cast<const __bf16 *>(p.v_pool) + (size_t)g * page_elems;
   const size_t phys_stride = (size_t)Hkv * page_elems;
-  const int c_tok = tid >> 4;              // + 16 * i
-  const int c_d0 = 8 * (tid & 15);
+  const int c_dg = tid & 15;
+  const int c_tq = tid >> 4;                // 0..15
+
+  // stage the block-table entries of every page the loads below can touch in LDS, so the
+  // pipelined loads depend on one LDS read instead of a global load.  The loads cover
+  // every token < L of the workgroup's tiles, which can run past kv_end in the last tile.
+  const int npages = (min(L, ntile * KT) + bs - 1) >> log2bs;
+  const bool tbl_in_lds = npages <= kTblLds;
+  if (tbl_in_lds)
+    for (int i = tid; i < npages; i += NTP) s_tbl[i] = trow[i];
+  __syncthreads();
 
   u32x4 rk[CHUNKS], rv[CHUNKS];
   auto load_regs = [&](int j) {
+    // the 4 tokens share one page (4 | bs)
+    const int t_first = j * KT + 4 * c_tq;
+    const bool any = t_first < L;
+    const int page = t_first >> log2bs;
+    const int phys = !any ? 0 : (tbl_in_lds ? s_tbl[page] : trow[page]);
+    const size_t base = (size_t)phys * phys_stride + (size_t)(t_first & (bs - 1)) * D + 8 * c_dg;
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      const int t = j * KT + c_tok + 16 * i;
-      if (t < L) {
-        const int phys = trow[t >> log2bs];
-        const size_t off = (size_t)phys * phys_stride + (size_t)(t & (bs - 1)) * D + c_d0;
-        rk[i] = *reinterpret_cast<const u32x4 *>(kpool + off);
-        rv[i] = *reinterpret_cast<const u32x4 *>(vpool + off);
+      if (t_first + i < L) {
+        rk[i] = *reinterpret_cast<const u32x4 *>(kpool + base + i * D);
+        rv[i] = *reinterpret_cast<const u32x4 *>(vpool + base + i * D);
       } else {
         rk[i] = u32x4{0u, 0u, 0u, 0u};
         rv[i] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto store_lds = [&]() {
+  auto store_lds = [&](int buf) {
+    char *kb = s_k[buf];
+    char *vb = s_vt[buf];
 #pragma unroll
-    for (int i = 0; i < CHUNKS; ++i) {
-      const int tk = c_tok + 16 * i;
-      *reinterpret_cast<u32x4 *>(s_k + tk * K_STRIDE + c_d0 * 2) = rk[i];
+    for (int i = 0; i < CHUNKS; ++i)
+      *reinterpret_cast<u32x4 *>(kb + (4 * c_tq + i) * K_STRIDE + c_dg * 16) = rk[i];
+    // V^T: for element d = 8*dg + e, the 4 tokens 4*tq .. +3 become one 8-byte group of row d,
+    // stored at group tq ^ (d >> 3) (XOR swizzle: conflict-free stores and loads)
+    const int vgrp = 8 * (c_tq ^ c_dg);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t dw = rv[i][w];
-        *reinterpret_cast<uint16_t *>(s_vt + (c_d0 + 2 * w) * V_STRIDE + tk * 2) = (uint16_t)(dw & 0xFFFFu);
-        *reinterpret_cast<uint16_t *>(s_vt + (c_d0 + 2 * w + 1) * V_STRIDE + tk * 2) = (uint16_t)(dw >> 16);
-      }
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo01 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x05040100u);   // e=2w:   t0 t1
+      const uint32_t lo23 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x05040100u);   //         t2 t3
+      const uint32_t hi01 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x07060302u);   // e=2w+1: t0 t1
+      const uint32_t hi23 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x07060302u);
+      *reinterpret_cast<u32x2 *>(vb + (8 * c_dg + 2 * w) * V_STRIDE + vgrp) = u32x2{lo01, lo23};
+      *reinterpret_cast<u32x2 *>(vb + (8 * c_dg + 2 * w + 1) * V_STRIDE + vgrp) = u32x2{hi01, hi23};
     }
   };
 
@@ -183,29 +209,36 @@ __global__ __launch_bounds__(NTP) void prefill_kernel(PrefillLaunch p) {
 #pragma unroll
     for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_regs(0);
-  for (int j = 0; j < ntile; ++j) {
-    __syncthreads();                       // every wave is done reading tile j-1
-    store_lds();
-    __syncthreads();
-    if (j + 1 < ntile) load_regs(j + 1);   // in flight while tile j is computed
+  auto compute = [&](int j) {
+    const char *kb = s_k[j & 1];
+    const char *vb = s_vt[j & 1];
     const int kv0 = j * KT;
-    if (!wave_active || kv0 > wave_last_pos) continue;    // fully masked for this wave
-
     // ---- S^T = K Q^T ----
     f32x4 s[4][2];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int qt2 = 0; qt2 < 2; ++qt2) s[tt][qt2] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments are read one k step ahead of the MFMAs that use them (the scheduling
+    // barriers keep the compiler from sinking the LDS reads next to their uses)
+    u32x4 ka[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      ka[0][tt] = *reinterpret_cast<const u32x4 *>(kb + (16 * tt + lq) * K_STRIDE + (8 * lg) * 2);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(s_k + (16 * tt + lq) * K_STRIDE + (32 * ks + 8 * lg) * 2);
-#pragma unroll
-        for (int qt2 = 0; qt2 < 2; ++qt2) s[tt][qt2] = mfma(a, qb[qt2][ks], s[tt][qt2]);
+        for (int tt = 0; tt < 4; ++tt)
+          ka[(ks + 1) & 1][tt] = *reinterpret_cast<const u32x4 *>(
+              kb + (16 * tt + lq) * K_STRIDE + (32 * (ks + 1) + 8 * lg) * 2);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int qt2 = 0; qt2 < 2; ++qt2) s[tt][qt2] = mfma(ka[ks & 1][tt], qb[qt2][ks], s[tt][qt2]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- scale, causal mask, online softmax (per query column) ----
     const bool diag = kv0 + KT - 1 > prior + q0;          // some element may be masked
@@ -255,24 +288,45 @@ __global__ __launch_bounds__(NTP) void prefill_kernel(PrefillLaunch p) {
           pv[i] = fast_exp2(s[2 * ks2][qt2][i] - m[qt2]);
           pv[4 + i] = fast_exp2(s[2 * ks2 + 1][qt2][i] - m[qt2]);
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) lsum[qt2] += bf16_round(pv[i]);
         pb[qt2][ks2] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                              pack_bf16(pv[6], pv[7])};
+        // the denominator sums the same bf16-rounded weights the product uses
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t pw = pb[qt2][ks2][w];
+          lsum[qt2] += __builtin_bit_cast(float, pw << 16) + __builtin_bit_cast(float, pw & 0xFFFF0000u);
+        }
       }
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const char *vrow = s_vt + (16 * dt + lq) * V_STRIDE + (32 * ks2 + 4 * lg) * 2;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 32);
+        const int vr = 16 * dt + lq;                 // row d of V^T; groups swizzled by d >> 3
+        const int sw = (vr >> 3) & 15;
+        const char *vrow = vb + vr * V_STRIDE;
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 8 * ((8 * ks2 + lg) ^ sw));
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 8 * ((8 * ks2 + 4 + lg) ^ sw));
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = mfma(a, pb[qt2][ks2], o[dt][qt2]);
       }
     }
+  };
+
+  // pipeline: tile j is computed from LDS while tile j+1 waits in LDS and tile j+2's
+  // global loads are in flight; one barrier per tile
+  load_regs(0);
+  store_lds(0);
+  if (ntile > 1) load_regs(1);
+  __syncthreads();
+  for (int j = 0; j < ntile; ++j) {
+    if (wave_active && j * KT <= wave_last_pos) compute(j);   // else fully masked for this wave
+    if (j + 1 < ntile) {
+      store_lds((j + 1) & 1);
+      if (j + 2 < ntile) load_regs(j + 2);
+    }
+    __syncthreads();
   }
 
   if (!wave_active) return;
@@ -289,8 +343,8 @@ __global__ __launch_bounds__(NTP) void prefill_kernel(PrefillLaunch p) {
     const size_t base = ((size_t)(q_begin + qi) * Hq + h) * D;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      f32x4 v = o[dt][qt2];
-      f32x4 r = {v[0] / lsum[qt2], v[1] / lsum[qt2], v[2] / lsum[qt2], v[3] / lsum[qt2]};
+      const f32x4 v = o[dt][qt2];
+      const f32x4 r = {v[0] / lsum[qt2], v[1] / lsum[qt2], v[2] / lsum[qt2], v[3] / lsum[qt2]};
       store4<OUT_BF16>(p.out, base + 16 * dt + 4 * lg, r);
     }
   }
