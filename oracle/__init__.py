@@ -35,6 +35,11 @@ scaled-dot-product softmax attention (readings listed in the design notes):
 with L = seq_lens[b] counting every cached token including the row's n new
 ones.  FP8 E4M3 KV values are ``decode(code) * scale[g]`` in fp64.
 
+Appending a step's new K/V (a scatter through per-token slot numbers, with
+E4M3 quantisation for an FP8 cache) is in ``append.py``; its pins are in
+``tests/test_oracle_append.py`` (encoder against its bit format, torch's
+``float8_e4m3fn`` cast, ties-to-even, saturation, scatter/gather round trip).
+
 Pins (see ``tests/test_oracle.py``): contiguous triple-loop brute force on
 tiny inputs, torch's fp64 ``scaled_dot_product_attention`` special case,
 closed-form invariants (constant V, single token, q = 0 mean, one-hot
@@ -43,6 +48,7 @@ the outcomeschool figure, and the full E4M3 code table against its bit
 format and torch's ``float8_e4m3fn``.
 """
 from .fp8_e4m3 import e4m3_decode_table, e4m3_decode
+from .append import append_kv, e4m3_encode, quantize_e4m3
 from .attention import (
     stored_to_f64,
     gather_kv,
@@ -53,6 +59,7 @@ from .attention import (
 )
 
 __all__ = [
-    "e4m3_decode_table", "e4m3_decode", "stored_to_f64", "gather_kv", "attend_rows",
+    "e4m3_decode_table", "e4m3_decode", "append_kv", "e4m3_encode", "quantize_e4m3",
+    "stored_to_f64", "gather_kv", "attend_rows",
     "paged_attention", "paged_attention_row", "paged_attention_workload",
 ]
