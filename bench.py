@@ -41,6 +41,10 @@ def parse():
                     help="decode work split into this many waves (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "append-fp8"],
+                    help="decode: the attention call of --workload (default); append / append-fp8: "
+                         "writing the mixed workload's 2,144 new tokens (96 decode + 8 x 256 prefill) "
+                         "into their cache slots, bf16 -> bf16 or bf16 -> FP8-E4M3")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed loop, run one device-to-device copy of this many MiB "
                          "(a plain copy kernel of known size, to calibrate HBM byte counters)")
@@ -106,6 +110,78 @@ def cpu_baseline(w, gpu_out, budget_s):
     }
 
 
+def bench_append(args):
+    """Time pa_append on the mixed workload's step: each row's new tokens go to their slots."""
+    import numpy as np
+    import torch
+
+    import pa_inputs
+    from paged_kv_attention_13_amd import binding
+
+    fp8 = args.op == "append-fp8"
+    L, ql = pa_inputs.workload_lengths(5)
+    w = pa_inputs.make_workload(name="append", seq_lens=L, q_lens=ql, block_size=16, seed=1005 + 7919,
+                                kv_fmt="fp8" if fp8 else "bf16")
+    bs = w.block_size
+    slots = []
+    for b in range(w.num_seqs):
+        for pos in range(int(L[b] - ql[b]), int(L[b])):
+            slots.append(int(w.block_table[b, pos // bs]) * bs + pos % bs)
+    slots = np.array(slots, dtype=np.int32)
+    T = len(slots)
+    rng = np.random.default_rng(77)
+    kn = pa_inputs.to_bf16_bits(rng.standard_normal((T, w.num_kv_heads, w.head_dim)).astype(np.float32))
+    vn = pa_inputs.to_bf16_bits(rng.standard_normal((T, w.num_kv_heads, w.head_dim)).astype(np.float32))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    k = dev(kn.view(np.int16)).view(torch.bfloat16)
+    v = dev(vn.view(np.int16)).view(torch.bfloat16)
+    if fp8:
+        kp, vp = dev(w.k_pool), dev(w.v_pool)
+        ks, vs = dev(w.k_scale), dev(w.v_scale)
+    else:
+        kp = dev(w.k_pool.view(np.int16)).view(torch.bfloat16)
+        vp = dev(w.v_pool.view(np.int16)).view(torch.bfloat16)
+        ks = vs = None
+    sm = dev(slots)
+    a = binding.make_append_args(k, v, sm, kp, vp, ks, vs)
+    import ctypes
+    call = lambda: binding.check(binding.LIB.pa_append(  # noqa: E731
+        ctypes.byref(a), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    # a launch lasts a few microseconds, about as long as an event pair's own overhead, so
+    # events bracket batches of `per` back-to-back launches on the launch stream
+    per = 10
+    nb = max(1, args.steps // per)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nb)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        for _ in range(per):
+            call()
+        e[1].record()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / (nb * per)
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) / per
+    nbytes = T * w.num_kv_heads * w.head_dim * 2 * (2 + (1 if fp8 else 2)) + 4 * T + (64 if fp8 else 0)
+    ach = nbytes / (k_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "paged KV append GB/s (new tokens written to their cache slots)",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": nb * per, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 -> fp8-e4m3" if fp8 else "bf16",
+        "data": "synthetic (seeded N(0,1) values, slots of the mixed workload's new tokens)",
+        "config": {"workload": f"append {T} tokens (96 decode + 8x256 prefill rows), 8 kv heads, "
+                               f"head_dim 128, bs 16, {'fp8' if fp8 else 'bf16'} pool", "tokens": T},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "append_kernel",
+                     "kernel_ms_mean": round(k_ms, 5), "bytes_per_launch": int(nbytes)},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -113,6 +189,10 @@ def main():
               "no exchange between GPUs; see the sharding note in the design document); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+
+    if args.op != "decode":
+        bench_append(args)
+        return
 
     import numpy as np
     import torch

@@ -130,6 +130,29 @@ typedef struct pa_mixed_args {
   int32_t max_q_len;           /* host-known upper bound on prefill-row q_len */
 } pa_mixed_args;
 
+/* Arguments of a KV append: write a step's new tokens into their cache slots
+ * (each step adds one key and value per token, taking a new block when the
+ * last one is full: "How does TensorRT-LLM work" (outcomeschool.com), section
+ * "The paged KV cache").  The host allocator chooses the slots. */
+typedef struct pa_append_args {
+  int32_t num_tokens;          /* T >= 0 new tokens */
+  int32_t num_kv_heads;        /* Hkv >= 1 */
+  int32_t head_dim;            /* D; 128 is supported */
+  int32_t block_size;          /* 16, 32, 64 or 128 */
+  int32_t num_blocks;          /* physical blocks in each pool */
+  int32_t src_dtype;           /* dtype of k and v: PA_F32 or PA_BF16 */
+  int32_t kv_dtype;            /* pool dtype: src_dtype, or PA_FP8_E4M3 */
+  const void *k;               /* [T][Hkv][D] */
+  const void *v;               /* [T][Hkv][D] */
+  const int32_t *slot_mapping; /* [T]: block * block_size + offset, or -1 to skip the token */
+  void *k_pool;                /* [num_blocks][Hkv][bs][D], kv_dtype */
+  void *v_pool;
+  const float *k_scale;        /* [Hkv], required iff kv_dtype == PA_FP8_E4M3: the code stored
+                                  is E4M3(x / k_scale[g]) with the quotient saturated to +-448
+                                  and rounded to nearest even */
+  const float *v_scale;        /* [Hkv], same rule */
+} pa_append_args;
+
 /* Launch plan of a decode call. */
 typedef struct pa_plan {
   int32_t num_workers;         /* worker waves the decode kernel runs */
@@ -170,6 +193,13 @@ pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
 /* Mixed in-flight batch: decode rows through the split-K decode kernels,
  * prefill-chunk rows through the MFMA causal tile kernel, all on `stream`. */
 pa_status pa_mixed(const pa_mixed_args *a, void *stream);
+
+/* Append: copy (or quantise) each token's [Hkv][D] K and V rows into
+ * pool[slot / bs][:, slot % bs, :].  Precondition: -1 <= slot_mapping[t] <
+ * num_blocks * block_size, no two tokens share a slot (pa_check_append_metadata
+ * verifies this on a host copy).  Queued on `stream`; allocates nothing. */
+pa_status pa_append(const pa_append_args *a, void *stream);
+pa_status pa_check_append_metadata(const pa_append_args *a_host);
 
 /* Synchronous CPU validation of the metadata preconditions above.  The
  * pointers block_table, seq_lens (and q_start_loc) must be HOST pointers;

@@ -21,8 +21,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: 
                 7: "PA_ERR_BAD_METADATA", 8: "PA_ERR_HIP"}
 
 EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_decode",
-            "pa_decode_partials", "pa_merge_partials", "pa_mixed", "pa_check_decode_metadata",
-            "pa_check_mixed_metadata", "pa_status_string", "pa_last_error"]
+            "pa_decode_partials", "pa_merge_partials", "pa_mixed", "pa_append", "pa_check_decode_metadata",
+            "pa_check_mixed_metadata", "pa_check_append_metadata", "pa_status_string", "pa_last_error"]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -63,6 +63,25 @@ class MixedArgs(ctypes.Structure):
     ]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("src_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p),
+        ("v_pool", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
+    ]
+
+
 class Plan(ctypes.Structure):
     _fields_ = [("num_workers", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
@@ -87,6 +106,8 @@ def _load():
         "pa_decode_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_merge_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_mixed": ([P(MixedArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_append": ([P(AppendArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_check_append_metadata": ([P(AppendArgs)], ctypes.c_int),
         "pa_check_decode_metadata": ([P(DecodeArgs)], ctypes.c_int),
         "pa_check_mixed_metadata": ([P(MixedArgs)], ctypes.c_int),
         "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -297,3 +318,39 @@ def check_mixed_metadata(block_table, seq_lens, q_start_loc, *, num_decode_rows:
     m.num_decode_rows = num_decode_rows
     m.max_q_len = max_q_len
     check(LIB.pa_check_mixed_metadata(ctypes.byref(m)))
+
+
+def make_append_args(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None) -> AppendArgs:
+    a = AppendArgs()
+    a.num_tokens = int(k.shape[0])
+    a.num_kv_heads = int(k.shape[1])
+    a.head_dim = int(k.shape[2])
+    a.block_size = int(k_pool.shape[2])
+    a.num_blocks = int(k_pool.shape[0])
+    a.src_dtype = dtype_code(k)
+    a.kv_dtype = dtype_code(k_pool)
+    a.k = _ptr(k)
+    a.v = _ptr(v)
+    a.slot_mapping = _ptr(slot_mapping)
+    a.k_pool = _ptr(k_pool)
+    a.v_pool = _ptr(v_pool)
+    a.k_scale = _ptr(k_scale)
+    a.v_scale = _ptr(v_scale)
+    return a
+
+
+def append(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None, stream=None) -> None:
+    """Write new tokens' K/V into their pool slots in place (``pa_append``)."""
+    a = make_append_args(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale)
+    check(LIB.pa_append(ctypes.byref(a), ctypes.c_void_p(_stream(stream))))
+
+
+def check_append_metadata(slot_mapping, *, num_kv_heads: int, head_dim: int, block_size: int,
+                          num_blocks: int, src_dtype: int = PA_BF16, kv_dtype: int = PA_BF16) -> None:
+    import numpy as np
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int32)
+    a = AppendArgs()
+    a.num_tokens, a.num_kv_heads, a.head_dim = len(sm), num_kv_heads, head_dim
+    a.block_size, a.num_blocks, a.src_dtype, a.kv_dtype = block_size, num_blocks, src_dtype, kv_dtype
+    a.slot_mapping = sm.ctypes.data
+    check(LIB.pa_check_append_metadata(ctypes.byref(a)))

@@ -48,6 +48,25 @@ pa_status pa_decode(const pa_decode_args *a, void *stream) {
   return hip_status(launch_merge(L, stream), "merge");
 }
 
+pa_status pa_append(const pa_append_args *a, void *stream) {
+  pa_status s = validate_append(a, true);
+  if (s != PA_OK || a->num_tokens == 0) return s;
+  AppendLaunch L{};
+  L.k = a->k;
+  L.v = a->v;
+  L.slot_mapping = a->slot_mapping;
+  L.k_pool = a->k_pool;
+  L.v_pool = a->v_pool;
+  L.k_scale = a->k_scale;
+  L.v_scale = a->v_scale;
+  L.num_tokens = a->num_tokens;
+  L.num_kv_heads = a->num_kv_heads;
+  L.block_size = a->block_size;
+  L.src_dtype = a->src_dtype;
+  L.kv_dtype = a->kv_dtype;
+  return hip_status(launch_append(L, stream), "append");
+}
+
 pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
   if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
   const pa_decode_args &b = a->base;

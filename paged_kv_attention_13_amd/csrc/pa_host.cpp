@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -158,6 +159,35 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   return PA_OK;
 }
 
+pa_status validate_append(const pa_append_args *a, bool need_device_pointers) {
+  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  if (a->num_tokens < 0) return set_error(PA_ERR_BAD_SHAPE, "num_tokens=%d < 0", a->num_tokens);
+  if (a->num_kv_heads < 1) return set_error(PA_ERR_BAD_SHAPE, "num_kv_heads=%d < 1", a->num_kv_heads);
+  if (a->head_dim != kHeadDim)
+    return set_error(PA_ERR_UNSUPPORTED, "head_dim=%d (supported: %d)", a->head_dim, kHeadDim);
+  if (!is_pow2_block(a->block_size))
+    return set_error(PA_ERR_UNSUPPORTED, "block_size=%d (supported: 16, 32, 64, 128)", a->block_size);
+  if (a->num_blocks < 1) return set_error(PA_ERR_BAD_SHAPE, "num_blocks=%d < 1", a->num_blocks);
+  if ((int64_t)a->num_blocks * a->block_size > INT32_MAX)
+    return set_error(PA_ERR_UNSUPPORTED, "num_blocks * block_size must fit in int32 slot numbers");
+  const bool src_ok = a->src_dtype == PA_F32 || a->src_dtype == PA_BF16;
+  const bool fp8 = a->kv_dtype == PA_FP8_E4M3;
+  if (!src_ok || !(a->kv_dtype == a->src_dtype || fp8))
+    return set_error(PA_ERR_BAD_DTYPE, "unsupported (src, kv) dtypes (%d, %d); supported: (f32, f32), "
+                     "(bf16, bf16), (f32|bf16, fp8_e4m3)", a->src_dtype, a->kv_dtype);
+  if (!fp8 && (a->k_scale || a->v_scale))
+    return set_error(PA_ERR_BAD_DTYPE, "k_scale/v_scale are only used with an FP8 KV cache");
+  if (need_device_pointers && a->num_tokens > 0) {
+    if (!a->k || !a->v || !a->slot_mapping || !a->k_pool || !a->v_pool)
+      return set_error(PA_ERR_NULL_POINTER, "k, v, slot_mapping, k_pool and v_pool are required");
+    if (fp8 && (!a->k_scale || !a->v_scale))
+      return set_error(PA_ERR_NULL_POINTER, "an FP8 KV cache needs k_scale and v_scale");
+    if (!aligned16(a->k) || !aligned16(a->v) || !aligned16(a->k_pool) || !aligned16(a->v_pool))
+      return set_error(PA_ERR_MISALIGNED, "k, v, k_pool and v_pool must be 16-byte aligned");
+  }
+  return PA_OK;
+}
+
 namespace {
 
 pa_status check_rows(const pa_decode_args *a, const int32_t *qsl, int n_dec, int max_q_len) {
@@ -245,6 +275,25 @@ pa_status pa_check_decode_metadata(const pa_decode_args *a) {
   if (a->num_seqs > 0 && (!a->seq_lens || !a->block_table))
     return set_error(PA_ERR_NULL_POINTER, "seq_lens and block_table host copies are required");
   return check_rows(a, nullptr, 0, 0);
+}
+
+pa_status pa_check_append_metadata(const pa_append_args *a) {
+  pa_status s = validate_append(a, false);
+  if (s != PA_OK) return s;
+  if (a->num_tokens > 0 && !a->slot_mapping)
+    return set_error(PA_ERR_NULL_POINTER, "slot_mapping host copy is required");
+  const int64_t nslots = (int64_t)a->num_blocks * a->block_size;
+  std::vector<char> used((size_t)nslots, 0);
+  for (int t = 0; t < a->num_tokens; ++t) {
+    const int32_t sl = a->slot_mapping[t];
+    if (sl < -1 || sl >= nslots)
+      return set_error(PA_ERR_BAD_METADATA, "slot_mapping[%d]=%d outside [-1, %lld)", t, sl, (long long)nslots);
+    if (sl >= 0) {
+      if (used[(size_t)sl]) return set_error(PA_ERR_BAD_METADATA, "slot %d written by two tokens", sl);
+      used[(size_t)sl] = 1;
+    }
+  }
+  return PA_OK;
 }
 
 pa_status pa_check_mixed_metadata(const pa_mixed_args *a) {

@@ -64,11 +64,27 @@ struct PrefillLaunch {
   float scale;
 };
 
+struct AppendLaunch {
+  const void *k;                 // [T][Hkv][D] src_dtype
+  const void *v;
+  const int32_t *slot_mapping;   // [T]
+  void *k_pool;                  // [num_blocks][Hkv][bs][D] kv_dtype
+  void *v_pool;
+  const float *k_scale;          // [Hkv] (FP8 only)
+  const float *v_scale;
+  int num_tokens;
+  int num_kv_heads;
+  int block_size;
+  int src_dtype;
+  int kv_dtype;
+};
+
 // Host helpers (pa_host.cpp).
 pa_status set_error(pa_status s, const char *fmt, ...);
 pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers);
 pa_status plan_decode(const pa_decode_args *a, pa_plan *plan);
 pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, DecodeLaunch *L);
+pa_status validate_append(const pa_append_args *a, bool need_device_pointers);
 size_t elem_bytes(int dtype);
 int tile_tokens(int kv_dtype);
 
@@ -77,6 +93,7 @@ int tile_tokens(int kv_dtype);
 int launch_decode_partials(const DecodeLaunch &L, void *stream);
 int launch_merge(const DecodeLaunch &L, void *stream);
 int launch_prefill(const PrefillLaunch &L, void *stream);
+int launch_append(const AppendLaunch &L, void *stream);
 const char *hip_error_name(int code);
 
 }  // namespace pa

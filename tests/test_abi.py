@@ -27,6 +27,7 @@ def test_header_declares_the_calls():
     names = _declared_functions()
     for n in ["pa_decode", "pa_mixed", "pa_decode_plan", "pa_decode_partials", "pa_merge_partials",
               "pa_check_decode_metadata", "pa_check_mixed_metadata", "pa_mixed_workspace_size",
+              "pa_append", "pa_check_append_metadata",
               "pa_status_string", "pa_last_error", "pa_abi_version"]:
         assert n in names
 
@@ -182,3 +183,46 @@ def test_mixed_metadata_checker(b):
 def test_status_strings(b):
     for code, name in b.STATUS_NAMES.items():
         assert b.LIB.pa_status_string(code).decode() == name
+
+
+def _append_args(b, **kw):
+    a = b.AppendArgs()
+    a.num_tokens, a.num_kv_heads, a.head_dim, a.block_size, a.num_blocks = 4, 8, 128, 16, 10
+    a.src_dtype = a.kv_dtype = b.PA_BF16
+    a.k = a.v = a.slot_mapping = a.k_pool = a.v_pool = 0x10000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_tokens=-1), "PA_ERR_BAD_SHAPE"),
+    (dict(num_kv_heads=0), "PA_ERR_BAD_SHAPE"),
+    (dict(head_dim=64), "PA_ERR_UNSUPPORTED"),
+    (dict(block_size=12), "PA_ERR_UNSUPPORTED"),
+    (dict(src_dtype=2), "PA_ERR_BAD_DTYPE"),
+    (dict(src_dtype=0), "PA_ERR_BAD_DTYPE"),              # f32 -> bf16 not offered
+    (dict(kv_dtype=2), "PA_ERR_NULL_POINTER"),            # fp8 without scales
+    (dict(k_scale=0x10000), "PA_ERR_BAD_DTYPE"),
+    (dict(slot_mapping=None), "PA_ERR_NULL_POINTER"),
+    (dict(v_pool=0x10002), "PA_ERR_MISALIGNED"),
+])
+def test_append_bad_arguments(b, kw, status):
+    a = _append_args(b, **kw)
+    assert b.STATUS_NAMES[b.LIB.pa_append(ctypes.byref(a), None)] == status, b.LIB.pa_last_error()
+
+
+def test_append_metadata_checker(b):
+    kw = dict(num_kv_heads=8, head_dim=128, block_size=16, num_blocks=4)
+    b.check_append_metadata([0, 17, -1, 63], **kw)
+    with pytest.raises(b.PagedAttentionError, match="outside"):
+        b.check_append_metadata([0, 64], **kw)
+    with pytest.raises(b.PagedAttentionError, match="outside"):
+        b.check_append_metadata([-2], **kw)
+    with pytest.raises(b.PagedAttentionError, match="two tokens"):
+        b.check_append_metadata([5, 6, 5], **kw)
+
+
+def test_append_struct_layout(b):
+    assert b.AppendArgs.k.offset == 32
+    assert ctypes.sizeof(b.AppendArgs) == 32 + 7 * 8
