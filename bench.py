@@ -35,8 +35,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5],
-                    help="named workload (3 = 55 x 8192 bf16 decode, the headline)")
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6],
+                    help="named workload (3 = 55 x 8192 bf16 decode, the headline; 6 = the same "
+                         "cache with 4 new tokens per row, speculative-decoding verify rows)")
     ap.add_argument("--num-workers", type=int, default=0,
                     help="decode work split into this many waves (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -210,10 +211,19 @@ def main():
 
     if mixed:
         n_dec = w.num_decode_rows
+        # rows after the decode rows with at most 32 query columns per kv head go to the
+        # multi-query (verify) kernel, the rest to the prefill-chunk kernel
+        group = w.num_q_heads // w.num_kv_heads
+        n_ver = 0
+        while n_dec + n_ver < w.num_seqs and w.q_lens[n_dec + n_ver] * group <= 32:
+            n_ver += 1
+        pre_q = w.q_lens[n_dec + n_ver:]
         m = binding.make_mixed_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
                                     d["q_start_loc"], w.scale, num_decode_rows=n_dec,
-                                    max_q_len=int(w.q_lens[n_dec:].max()), max_seq_len=w.max_seq_len,
-                                    out=out, num_workers=args.num_workers)
+                                    max_q_len=int(pre_q.max()) if len(pre_q) else 1,
+                                    max_seq_len=w.max_seq_len, out=out, num_workers=args.num_workers,
+                                    num_verify_rows=n_ver,
+                                    max_verify_q_len=int(w.q_lens[n_dec:n_dec + n_ver].max()) if n_ver else 0)
         nbytes = binding.mixed_workspace_bytes(m)
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
         m.base.workspace, m.base.workspace_bytes = ws.data_ptr(), ws.numel()
@@ -233,6 +243,7 @@ def main():
         a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
         stages = (lambda: binding.decode_partials(a), lambda: binding.merge_partials(a))
         step = None
+        n_dec, n_ver = w.num_seqs, 0
 
     def run_step(evs=None):
         if stages is None:
@@ -311,7 +322,10 @@ def main():
                    "context_tokens": int(w.seq_lens.sum()), "max_context": w.max_seq_len,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "kv_dtype": w.kv_fmt,
-                   "decode_workers": pl.num_workers, "tile_tokens": pl.tile_tokens},
+                   "decode_rows": w.num_decode_rows if mixed else w.num_seqs,
+                   "verify_rows": n_ver if mixed else 0,
+                   "decode_workers": pl.num_workers if pl.num_workers and (not mixed or n_dec) else None,
+                   "tile_tokens": pl.tile_tokens},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_per_step * 1e-3), 1),

@@ -18,7 +18,10 @@
  *   - prefill chunks mixed with decode rows in one pass: same page, section
  *     "In-flight batching and the scheduler";
  *   - an FP8 KV cache: same page, section "Quantization: fewer bytes per
- *     weight and per cached token".
+ *     weight and per cached token";
+ *   - rows that check a few drafted tokens in one pass (speculative
+ *     decoding): same page and "How does TensorRT-LLM work", sections
+ *     "Speculative decoding".
  *
  * Operation (one layer).  For row b with L = seq_lens[b] cached tokens
  * (including the row's n new ones), new query i in [0, n), and query head h
@@ -46,10 +49,11 @@
  * Errors.  Every host-checkable problem returns a status before anything is
  * launched: null pointers, misalignment (16 bytes for q, pools, out,
  * workspace), dtype combinations, Hq % Hkv, supported head_dim / block size /
- * group size, workspace too small, num_decode_rows > num_seqs.  Launch
+ * group size, workspace too small, row classes that do not fit num_seqs.  Launch
  * failures return PA_ERR_HIP.  The device-resident metadata is a
  * PRECONDITION that the kernels do not re-check:
  *     1 <= q_len_b <= L_b <= max_seq_len <= max_blocks_per_seq * bs,
+ *     q_len_b within its class's bound (1, max_verify_q_len, max_q_len),
  *     0 <= block_table[b][j] < num_blocks for j < ceil(L_b / bs).
  * pa_check_decode_metadata / pa_check_mixed_metadata verify it on host copies.
  * Table entries at j >= ceil(L_b / bs), pool slots past L_b in a row's last
@@ -67,7 +71,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 /* Element types.  Supported (q, kv, out) combinations:
  *   (F32, F32, F32|BF16), (BF16, BF16, BF16|F32), (BF16, FP8_E4M3, BF16|F32). */
@@ -118,16 +122,26 @@ typedef struct pa_decode_args {
   size_t workspace_bytes;
 } pa_decode_args;
 
-/* Arguments of a mixed in-flight batch: rows [0, num_decode_rows) are decode
- * rows (q_len 1), the remaining rows are chunked-prefill rows whose q_len new
- * tokens are already appended to the cache. */
+/* Arguments of a mixed in-flight batch, rows in three classes, in this order:
+ *   [0, D)        decode rows (q_len 1), D = num_decode_rows;
+ *   [D, D + V)    verify rows (1 <= q_len <= max_verify_q_len), V = num_verify_rows:
+ *                 a few new tokens per row, e.g. the drafted tokens of
+ *                 speculative decoding;
+ *   [D + V, B)    chunked-prefill rows (q_len <= max_q_len).
+ * Every row's q_len new tokens are already appended to the cache.  The class
+ * only chooses the kernel; the result is the same attention for all rows. */
 typedef struct pa_mixed_args {
   pa_decode_args base;         /* base.q and base.out are [total_q][Hq][D];
-                                  base.seq_lens counts the row's new tokens too */
+                                  base.seq_lens counts the row's new tokens too;
+                                  base.num_workers (if nonzero) also sets the
+                                  verify rows' work split */
   const int32_t *q_start_loc;  /* [num_seqs + 1] */
   int32_t total_q;             /* q_start_loc[num_seqs] */
   int32_t num_decode_rows;     /* rows with q_len == 1 placed first */
   int32_t max_q_len;           /* host-known upper bound on prefill-row q_len */
+  int32_t num_verify_rows;     /* rows following the decode rows (0 = none) */
+  int32_t max_verify_q_len;    /* host-known upper bound on verify-row q_len; with
+                                  G = Hq/Hkv, max_verify_q_len * G <= 32 */
 } pa_mixed_args;
 
 /* Arguments of a KV append: write a step's new tokens into their cache slots
@@ -191,7 +205,10 @@ pa_status pa_decode_partials(const pa_decode_args *a, void *stream);
 pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
 
 /* Mixed in-flight batch: decode rows through the split-K decode kernels,
- * prefill-chunk rows through the MFMA causal tile kernel, all on `stream`. */
+ * verify rows through the split-K MFMA multi-query kernels (bf16 q and KV),
+ * prefill-chunk rows through the MFMA causal tile kernel (bf16 q and KV), all
+ * on `stream`.  The workspace (pa_mixed_workspace_size) holds the decode rows'
+ * split records and partials followed by the verify rows'. */
 pa_status pa_mixed(const pa_mixed_args *a, void *stream);
 
 /* Append: copy (or quantise) each token's [Hkv][D] K and V rows into

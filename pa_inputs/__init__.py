@@ -275,6 +275,7 @@ WORKLOAD_NAMES = {
     3: "decode bf16 B55 ctx8192 bs64",
     4: "decode fp8kv B128 ctxlogU[128,8192] bs16",
     5: "mixed bf16 8x256-chunk prefill + 96 decode bs16",
+    6: "verify bf16 B55 ctx8192 q4 bs64",
 }
 
 
@@ -298,11 +299,15 @@ def workload_lengths(i: int, seed: Optional[int] = None):
         L = np.concatenate([dec, prior + 256]).astype(np.int32)
         ql = np.concatenate([np.ones(96, np.int32), np.full(8, 256, np.int32)])
         return L, ql
+    if i == 6:
+        # speculative decoding: every row checks 4 drafted tokens in one pass; the long
+        # context of workload 3, so its KV bytes equal that workload's
+        return np.full(55, 8192, np.int32), np.full(55, 4, np.int32)
     raise ValueError(i)
 
 
 def make_config(i: int, seed: Optional[int] = None, poison_unused: bool = False) -> Workload:
-    """Named workload i (1..5) at full size."""
+    """Named workload i (1..6) at full size."""
     seed = (1000 + i) if seed is None else seed
     L, ql = workload_lengths(i, seed)
     common = dict(name=WORKLOAD_NAMES[i], seq_lens=L, q_lens=ql, seed=seed + 7919,
@@ -317,4 +322,6 @@ def make_config(i: int, seed: Optional[int] = None, poison_unused: bool = False)
         return make_workload(block_size=16, kv_fmt="fp8", **common)
     if i == 5:
         return make_workload(block_size=16, **common)
+    if i == 6:
+        return make_workload(block_size=64, **common)
     raise ValueError(i)

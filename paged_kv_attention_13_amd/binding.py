@@ -60,6 +60,8 @@ class MixedArgs(ctypes.Structure):
         ("total_q", ctypes.c_int32),
         ("num_decode_rows", ctypes.c_int32),
         ("max_q_len", ctypes.c_int32),
+        ("num_verify_rows", ctypes.c_int32),
+        ("max_verify_q_len", ctypes.c_int32),
     ]
 
 
@@ -242,7 +244,8 @@ def decode_args_call(args: DecodeArgs, stream=None) -> None:
 
 def make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *,
                     num_decode_rows: int, max_q_len: int, max_seq_len: int, out=None,
-                    num_workers: int = 0) -> MixedArgs:
+                    num_workers: int = 0, num_verify_rows: int = 0,
+                    max_verify_q_len: int = 0) -> MixedArgs:
     m = MixedArgs()
     m.base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
                               out=out, num_workers=num_workers)
@@ -250,6 +253,8 @@ def make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale
     m.total_q = int(q.shape[0])
     m.num_decode_rows = int(num_decode_rows)
     m.max_q_len = int(max_q_len)
+    m.num_verify_rows = int(num_verify_rows)
+    m.max_verify_q_len = int(max_verify_q_len)
     return m
 
 
@@ -261,13 +266,15 @@ def mixed_workspace_bytes(m: MixedArgs) -> int:
 
 def mixed(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *, num_decode_rows: int,
           max_q_len: int, max_seq_len: int, out=None, out_dtype=None, num_workers: int = 0,
-          workspace=None, stream=None):
-    """Mixed decode + chunked-prefill batch (``pa_mixed``).  Returns ``out`` [total_q, Hq, D]."""
+          num_verify_rows: int = 0, max_verify_q_len: int = 0, workspace=None, stream=None):
+    """Mixed batch (``pa_mixed``): decode rows, then verify rows, then prefill-chunk rows.
+    Returns ``out`` [total_q, Hq, D]."""
     if out is None:
         out = _alloc_out(q, out_dtype)
     m = make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale,
                         num_decode_rows=num_decode_rows, max_q_len=max_q_len,
-                        max_seq_len=max_seq_len, out=out, num_workers=num_workers)
+                        max_seq_len=max_seq_len, out=out, num_workers=num_workers,
+                        num_verify_rows=num_verify_rows, max_verify_q_len=max_verify_q_len)
     if workspace is None:
         workspace = _alloc_workspace(mixed_workspace_bytes(m), q.device)
     if workspace is not None:
@@ -300,7 +307,8 @@ def check_decode_metadata(block_table, seq_lens, *, num_q_heads: int, num_kv_hea
 
 def check_mixed_metadata(block_table, seq_lens, q_start_loc, *, num_decode_rows: int, max_q_len: int,
                          num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
-                         num_blocks: int, max_seq_len: int) -> None:
+                         num_blocks: int, max_seq_len: int, num_verify_rows: int = 0,
+                         max_verify_q_len: int = 0) -> None:
     import numpy as np
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
@@ -317,6 +325,8 @@ def check_mixed_metadata(block_table, seq_lens, q_start_loc, *, num_decode_rows:
     m.total_q = int(qs[-1])
     m.num_decode_rows = num_decode_rows
     m.max_q_len = max_q_len
+    m.num_verify_rows = num_verify_rows
+    m.max_verify_q_len = max_verify_q_len
     check(LIB.pa_check_mixed_metadata(ctypes.byref(m)))
 
 

@@ -68,36 +68,27 @@ pa_status pa_append(const pa_append_args *a, void *stream) {
 }
 
 pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
-  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
-  const pa_decode_args &b = a->base;
-  pa_status s = validate_decode(&b, true);
+  pa_decode_args d;
+  pa_plan plan;
+  int verify_workers = 0;
+  size_t verify_offset = 0, total = 0;
+  pa_status s = plan_mixed(a, true, &d, &plan, &verify_workers, &verify_offset, &total);
   if (s != PA_OK) return s;
-  if (a->num_decode_rows < 0 || a->num_decode_rows > b.num_seqs)
-    return set_error(PA_ERR_BAD_SHAPE, "num_decode_rows=%d outside [0, num_seqs=%d]",
-                     a->num_decode_rows, b.num_seqs);
-  const int n_pre = b.num_seqs - a->num_decode_rows;
-  if (b.num_seqs > 0 && !a->q_start_loc)
-    return set_error(PA_ERR_NULL_POINTER, "q_start_loc is required");
-  if (a->total_q < b.num_seqs)
-    return set_error(PA_ERR_BAD_SHAPE, "total_q=%d < num_seqs=%d", a->total_q, b.num_seqs);
-  if (n_pre > 0) {
-    if (a->max_q_len < 1 || a->max_q_len > b.max_seq_len)
-      return set_error(PA_ERR_BAD_SHAPE, "max_q_len=%d outside [1, max_seq_len=%d]", a->max_q_len,
-                       b.max_seq_len);
-    if (b.kv_dtype != PA_BF16)
-      return set_error(PA_ERR_UNSUPPORTED, "prefill-chunk rows need a bf16 KV cache and bf16 q");
-  }
+  const pa_decode_args &b = a->base;
+  if (total > 0 && (!b.workspace || b.workspace_bytes < total))
+    return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, the batch needs %zu",
+                     b.workspace ? b.workspace_bytes : (size_t)0, total);
+  const int n_ver = a->num_verify_rows;
+  const int n_pre = b.num_seqs - a->num_decode_rows - n_ver;
   // decode rows: a decode call over rows [0, num_decode_rows), whose q and out
   // rows are the first num_decode_rows rows of the packed q/out.
-  pa_decode_args d = b;
-  d.num_seqs = a->num_decode_rows;
-  pa_plan plan;
   DecodeLaunch L;
-  plan_decode(&d, &plan);
   if (d.num_seqs > 0) {
     s = make_decode_launch(&d, plan, &L);
     if (s != PA_OK) return s;
   }
+  VerifyLaunch V;
+  if (n_ver > 0) make_verify_launch(a, verify_workers, verify_offset, &V);
   // validation is complete: queue the work
   if (n_pre > 0) {
     PrefillLaunch P{};
@@ -108,7 +99,7 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.seq_lens = b.seq_lens;
     P.q_start_loc = a->q_start_loc;
     P.out = b.out;
-    P.first_row = a->num_decode_rows;
+    P.first_row = a->num_decode_rows + n_ver;
     P.num_rows = n_pre;
     P.num_q_heads = b.num_q_heads;
     P.num_kv_heads = b.num_kv_heads;
@@ -118,6 +109,12 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.out_dtype = b.out_dtype;
     P.scale = b.scale;
     s = hip_status(launch_prefill(P, stream), "prefill");
+    if (s != PA_OK) return s;
+  }
+  if (n_ver > 0) {
+    s = hip_status(launch_verify_partials(V, stream), "verify");
+    if (s != PA_OK) return s;
+    s = hip_status(launch_verify_merge(V, stream), "verify merge");
     if (s != PA_OK) return s;
   }
   if (d.num_seqs > 0) {

@@ -159,6 +159,101 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   return PA_OK;
 }
 
+pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decode_args *dec,
+                     pa_plan *dec_plan, int *verify_workers, size_t *verify_offset,
+                     size_t *total_bytes) {
+  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  const pa_decode_args &b = a->base;
+  pa_status s = validate_decode(&b, need_device_pointers);
+  if (s != PA_OK) return s;
+  const int B = b.num_seqs;
+  const int nd = a->num_decode_rows;
+  const int nv = a->num_verify_rows;
+  if (nd < 0 || nv < 0 || (int64_t)nd + nv > B)
+    return set_error(PA_ERR_BAD_SHAPE, "num_decode_rows=%d, num_verify_rows=%d do not fit num_seqs=%d", nd,
+                     nv, B);
+  const int n_pre = B - nd - nv;
+  if (B > 0 && need_device_pointers && !a->q_start_loc)
+    return set_error(PA_ERR_NULL_POINTER, "q_start_loc is required");
+  if (B > 0 && a->total_q < B)
+    return set_error(PA_ERR_BAD_SHAPE, "total_q=%d < num_seqs=%d", a->total_q, B);
+  const int G = b.num_q_heads / b.num_kv_heads;
+  if (nv > 0) {
+    if (a->max_verify_q_len < 1 || (int64_t)a->max_verify_q_len * G > kVerifyMaxCols)
+      return set_error(PA_ERR_UNSUPPORTED,
+                       "max_verify_q_len=%d with group size %d: need 1 <= max_verify_q_len * group <= %d",
+                       a->max_verify_q_len, G, kVerifyMaxCols);
+    if (a->max_verify_q_len > b.max_seq_len)
+      return set_error(PA_ERR_BAD_SHAPE, "max_verify_q_len=%d > max_seq_len=%d", a->max_verify_q_len,
+                       b.max_seq_len);
+    if (b.kv_dtype != PA_BF16)
+      return set_error(PA_ERR_UNSUPPORTED, "verify rows need a bf16 KV cache and bf16 q");
+  }
+  if (n_pre > 0) {
+    if (a->max_q_len < 1 || a->max_q_len > b.max_seq_len)
+      return set_error(PA_ERR_BAD_SHAPE, "max_q_len=%d outside [1, max_seq_len=%d]", a->max_q_len,
+                       b.max_seq_len);
+    if (b.kv_dtype != PA_BF16)
+      return set_error(PA_ERR_UNSUPPORTED, "prefill-chunk rows need a bf16 KV cache and bf16 q");
+  }
+  *dec = b;
+  dec->num_seqs = nd;
+  plan_decode(dec, dec_plan);
+  *verify_workers = 0;
+  *verify_offset = round_up(dec_plan->workspace_bytes, 256);
+  size_t vbytes = 0;
+  if (nv > 0) {
+    const int64_t units = (int64_t)nv * b.num_kv_heads;
+    int nw = b.num_workers;
+    if (nw == 0) {
+      const int64_t tiles_upper = units * ((b.max_seq_len + kVerifyTile - 1) / kVerifyTile);
+      nw = (int)std::min<int64_t>(kVerifyMaxWorkers,
+                                  std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) / kMinTilesPerWorker));
+    }
+    *verify_workers = nw;
+    const size_t slots = (size_t)(units + nw) * (size_t)(a->max_verify_q_len * G);
+    vbytes = round_up(2 * (size_t)units * sizeof(int32_t), 256) + 2 * round_up(slots * sizeof(float), 256) +
+             round_up(slots * kHeadDim * sizeof(float), 256);
+  }
+  *total_bytes = nv > 0 ? *verify_offset + vbytes : dec_plan->workspace_bytes;
+  return PA_OK;
+}
+
+pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_offset, VerifyLaunch *V) {
+  std::memset(V, 0, sizeof *V);
+  const pa_decode_args &b = a->base;
+  const int G = b.num_q_heads / b.num_kv_heads;
+  V->q = b.q;
+  V->k_pool = b.k_pool;
+  V->v_pool = b.v_pool;
+  V->block_table = b.block_table;
+  V->seq_lens = b.seq_lens;
+  V->q_start_loc = a->q_start_loc;
+  V->out = b.out;
+  V->first_row = a->num_decode_rows;
+  V->num_rows = a->num_verify_rows;
+  V->num_q_heads = b.num_q_heads;
+  V->num_kv_heads = b.num_kv_heads;
+  V->block_size = b.block_size;
+  V->max_blocks_per_seq = b.max_blocks_per_seq;
+  V->num_workers = workers;
+  V->slot_cols = a->max_verify_q_len * G;
+  V->out_dtype = b.out_dtype;
+  V->scale = b.scale;
+  const size_t units = (size_t)a->num_verify_rows * b.num_kv_heads;
+  const size_t slots = (units + workers) * (size_t)V->slot_cols;
+  char *base = static_cast<char *>(b.workspace) + verify_offset;
+  V->seg_first = reinterpret_cast<int32_t *>(base);
+  V->seg_count = V->seg_first + units;
+  base += round_up(2 * units * sizeof(int32_t), 256);
+  V->part_m = reinterpret_cast<float *>(base);
+  base += round_up(slots * sizeof(float), 256);
+  V->part_l = reinterpret_cast<float *>(base);
+  base += round_up(slots * sizeof(float), 256);
+  V->part_acc = reinterpret_cast<float *>(base);
+  return PA_OK;
+}
+
 pa_status validate_append(const pa_append_args *a, bool need_device_pointers) {
   if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
   if (a->num_tokens < 0) return set_error(PA_ERR_BAD_SHAPE, "num_tokens=%d < 0", a->num_tokens);
@@ -190,7 +285,8 @@ pa_status validate_append(const pa_append_args *a, bool need_device_pointers) {
 
 namespace {
 
-pa_status check_rows(const pa_decode_args *a, const int32_t *qsl, int n_dec, int max_q_len) {
+pa_status check_rows(const pa_decode_args *a, const int32_t *qsl, int n_dec, int n_ver, int max_ver_q,
+                     int max_q_len) {
   const int bs = a->block_size;
   for (int b = 0; b < a->num_seqs; ++b) {
     const int L = a->seq_lens[b];
@@ -213,7 +309,10 @@ pa_status check_rows(const pa_decode_args *a, const int32_t *qsl, int n_dec, int
         return set_error(PA_ERR_BAD_METADATA, "row %d: q_len=%d outside [1, seq_len=%d]", b, ql, L);
       if (b < n_dec && (ql != 1 || qsl[b] != b))
         return set_error(PA_ERR_BAD_METADATA, "decode row %d must have q_len 1 at q index %d", b, b);
-      if (b >= n_dec && ql > max_q_len)
+      if (b >= n_dec && b < n_dec + n_ver && ql > max_ver_q)
+        return set_error(PA_ERR_BAD_METADATA, "verify row %d: q_len=%d > max_verify_q_len=%d", b, ql,
+                         max_ver_q);
+      if (b >= n_dec + n_ver && ql > max_q_len)
         return set_error(PA_ERR_BAD_METADATA, "row %d: q_len=%d > max_q_len=%d", b, ql, max_q_len);
     }
   }
@@ -256,17 +355,12 @@ pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan) {
 
 pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes) {
   if (!a || !bytes) return set_error(PA_ERR_NULL_POINTER, "argument is NULL");
-  pa_decode_args d = a->base;
-  if (a->num_decode_rows < 0 || a->num_decode_rows > a->base.num_seqs)
-    return set_error(PA_ERR_BAD_SHAPE, "num_decode_rows=%d outside [0, num_seqs=%d]",
-                     a->num_decode_rows, a->base.num_seqs);
-  d.num_seqs = a->num_decode_rows;
-  pa_status s = validate_decode(&d, false);
-  if (s != PA_OK) return s;
+  pa_decode_args d;
   pa_plan p;
-  plan_decode(&d, &p);
-  *bytes = p.workspace_bytes;
-  return PA_OK;
+  int vw = 0;
+  size_t voff = 0;
+  pa_status s = plan_mixed(a, false, &d, &p, &vw, &voff, bytes);
+  return s;
 }
 
 pa_status pa_check_decode_metadata(const pa_decode_args *a) {
@@ -274,7 +368,7 @@ pa_status pa_check_decode_metadata(const pa_decode_args *a) {
   if (s != PA_OK) return s;
   if (a->num_seqs > 0 && (!a->seq_lens || !a->block_table))
     return set_error(PA_ERR_NULL_POINTER, "seq_lens and block_table host copies are required");
-  return check_rows(a, nullptr, 0, 0);
+  return check_rows(a, nullptr, 0, 0, 0, 0);
 }
 
 pa_status pa_check_append_metadata(const pa_append_args *a) {
@@ -298,13 +392,15 @@ pa_status pa_check_append_metadata(const pa_append_args *a) {
 
 pa_status pa_check_mixed_metadata(const pa_mixed_args *a) {
   if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
-  pa_status s = validate_decode(&a->base, false);
+  pa_decode_args d;
+  pa_plan p;
+  int vw = 0;
+  size_t voff = 0, total = 0;
+  pa_status s = plan_mixed(a, false, &d, &p, &vw, &voff, &total);
   if (s != PA_OK) return s;
   const int B = a->base.num_seqs;
   if (B > 0 && (!a->base.seq_lens || !a->base.block_table || !a->q_start_loc))
     return set_error(PA_ERR_NULL_POINTER, "seq_lens, block_table and q_start_loc host copies are required");
-  if (a->num_decode_rows < 0 || a->num_decode_rows > B)
-    return set_error(PA_ERR_BAD_SHAPE, "num_decode_rows=%d outside [0, %d]", a->num_decode_rows, B);
   if (B > 0) {
     if (a->q_start_loc[0] != 0)
       return set_error(PA_ERR_BAD_METADATA, "q_start_loc[0]=%d != 0", a->q_start_loc[0]);
@@ -312,7 +408,8 @@ pa_status pa_check_mixed_metadata(const pa_mixed_args *a) {
       return set_error(PA_ERR_BAD_METADATA, "q_start_loc[%d]=%d != total_q=%d", B, a->q_start_loc[B],
                        a->total_q);
   }
-  return check_rows(&a->base, a->q_start_loc, a->num_decode_rows, a->max_q_len);
+  return check_rows(&a->base, a->q_start_loc, a->num_decode_rows, a->num_verify_rows, a->max_verify_q_len,
+                    a->max_q_len);
 }
 
 }  // extern "C"

@@ -17,6 +17,9 @@ constexpr int kTargetCUs = 256;          // MI355X compute units (grid planning 
 constexpr int kWorkersPerCU = 8;         // resident decode waves per CU (2 per SIMD)
 constexpr int kMaxWorkers = kTargetCUs * kWorkersPerCU;
 constexpr int kMinTilesPerWorker = 4;    // below this, fewer workers are launched
+constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
+constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
+constexpr int kVerifyMaxWorkers = kTargetCUs * 4;   // one verify wave per SIMD
 
 // Everything a decode launch needs, resolved on the host.
 struct DecodeLaunch {
@@ -64,6 +67,31 @@ struct PrefillLaunch {
   float scale;
 };
 
+struct VerifyLaunch {
+  const void *q;                 // [total_q][Hq][D] bf16
+  const void *k_pool;            // bf16 pools
+  const void *v_pool;
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+  const int32_t *q_start_loc;
+  void *out;
+  int32_t *seg_first;            // [rows*Hkv] first worker covering each (row, kv head) unit
+  int32_t *seg_count;            // [rows*Hkv] number of workers covering it
+  float *part_m;                 // [(rows*Hkv + workers) * slot_cols] partial slot (unit + worker), column
+  float *part_l;
+  float *part_acc;               // [... * slot_cols][D]
+  int first_row;                 // first verify row
+  int num_rows;                  // verify rows
+  int num_q_heads;
+  int num_kv_heads;
+  int block_size;
+  int max_blocks_per_seq;
+  int num_workers;
+  int slot_cols;                 // max_verify_q_len * G (<= kVerifyMaxCols)
+  int out_dtype;
+  float scale;
+};
+
 struct AppendLaunch {
   const void *k;                 // [T][Hkv][D] src_dtype
   const void *v;
@@ -86,14 +114,23 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan);
 pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, DecodeLaunch *L);
 pa_status validate_append(const pa_append_args *a, bool need_device_pointers);
 size_t elem_bytes(int dtype);
+// Checks the pa_mixed row classes; fills the decode and verify sub-plans and the
+// total workspace size (decode part first, then the verify part at verify_offset).
+pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decode_args *dec,
+                     pa_plan *dec_plan, int *verify_workers, size_t *verify_offset,
+                     size_t *total_bytes);
+pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_offset,
+                             VerifyLaunch *V);
 int tile_tokens(int kv_dtype);
 
-// Kernel launchers (decode.hip, prefill.hip).  Return 0 on success, else the
+// Kernel launchers (decode.hip, prefill.hip, verify.hip, append.hip).  Return 0 on success, else the
 // HIP error code of the failed launch.
 int launch_decode_partials(const DecodeLaunch &L, void *stream);
 int launch_merge(const DecodeLaunch &L, void *stream);
 int launch_prefill(const PrefillLaunch &L, void *stream);
 int launch_append(const AppendLaunch &L, void *stream);
+int launch_verify_partials(const VerifyLaunch &V, void *stream);
+int launch_verify_merge(const VerifyLaunch &V, void *stream);
 const char *hip_error_name(int code);
 
 }  // namespace pa

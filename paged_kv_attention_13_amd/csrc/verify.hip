@@ -1,0 +1,489 @@
+// Multi-query "verify" rows over a paged KV cache on gfx950 MFMA.
+//
+// What is computed: rows that carry a handful of new tokens (the draft tokens
+// of speculative decoding, all checked by the target model in one pass:
+// "How does TensorRT-LLM work", outcomeschool.com, section "Speculative
+// decoding"; "TensorRT-LLM, in depth", aicassindra.com, section "Speculative
+// decoding").  Their K/V are already in the cache: with L cached tokens and n
+// new ones, new token i sits at position L - n + i and attends to every token
+// up to and including itself.
+//
+// Such rows are decode-like -- each reads its whole cache once, so the pass is
+// HBM-bound -- but carry n x (Hq/Hkv) query columns per kv head (up to 32),
+// too many for the VALU dot products of the decode kernel.  Here the two
+// contractions run on the matrix cores and everything else follows the decode
+// kernel: the flattened (row, kv head, 32-token tile) work is cut into equal
+// ranges, one per worker wave; a unit covered by one wave is finished in
+// place, a unit cut by range boundaries leaves one (m, l, acc) partial per
+// piece and query column for the log-sum-exp merge kernel.
+//
+// Per 32-token tile and wave (C = 16 or 32 query columns, column c = query
+// c / G, head c % G of the kv head's group):
+//   S^T = K Q^T   : 2 x C/16 x 4 v_mfma_f32_16x16x32_bf16.  The A operand
+//                   (16 tokens x 32 head-dim elements) is exactly what a lane
+//                   loads from the page: 16 contiguous bytes of one token row,
+//                   so K goes from HBM straight into MFMA registers.
+//   online softmax per column in fp32 (log2 domain, lazy rescale)
+//   O^T += V^T P^T: 8 x C/16 v_mfma_f32_16x16x32_bf16, plus C/16 more against
+//                   a row of ones for the softmax denominators.  P^T is already in
+//                   B-operand order in the S^T accumulators (k slot 8q + j of a
+//                   lane group q is token 4q + j, or 16 + 4q + j - 4 for j >= 4).
+//                   V^T goes through a wave-private 8 KB LDS tile: each lane
+//                   loads 4 consecutive tokens x 8 elements twice, transposes
+//                   them with byte permutes and writes 16-byte groups at a
+//                   swizzled position (conflict-free for the writes and for
+//                   the MFMA-operand reads).
+// Three register sets keep two tiles' loads in flight while one is computed;
+// one wave per SIMD (up to 512 registers).  Tokens at or past the row's end
+// are excluded by select and their V zeroed before the transpose, so NaN in
+// unused pool slots cannot leak.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = kHeadDim;            // 128
+constexpr int TILE = kVerifyTile;      // 32 tokens
+constexpr int NW = kWavesPerBlock;     // 4 independent waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int VT_BYTES = D * TILE * 2; // one wave's V^T tile: 8 KB
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;
+constexpr float kSlack = 8.0f;
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ long long readlane64(long long v, int k) {
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xFFFFFFFFLL), k);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), k);
+  return ((long long)hi << 32) | (unsigned int)lo;
+}
+
+// Byte offset of the 16-byte group gi (k slots 8 gi .. 8 gi + 7) of V^T row d in
+// a wave's tile.  Rows are taken four at a time (256 bytes = all 64 banks); within
+// such a block the row picks the bank quarter and the group is XOR-ed with the
+// block index, so that both the transposing writes (lanes of a pass hold rows
+// 8 dg + e for four dg, groups 0..3) and the operand reads (rows 16 db + 0..15,
+// one group) touch 16 distinct quarters x groups.
+__device__ __forceinline__ int vt_offset(int d, int gi) {
+  const int blk = d >> 2;
+  const int quarter = ((d & 3) + (blk >> 1)) & 3;
+  return blk * 256 + (4 * quarter + (gi ^ (blk & 3))) * 16;
+}
+
+// Keeps the compiler from moving this wave's LDS accesses across the point;
+// the LDS itself serves one wave's accesses in issue order.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool OUT_BF16>
+__device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
+  if constexpr (OUT_BF16) {
+    u32x2 w = {pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+    *reinterpret_cast<u32x2 *>(static_cast<__bf16 *>(out) + idx) = w;
+  } else {
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + idx) = v;
+  }
+}
+
+// NCB: 16-column blocks of query columns (1: up to 16 columns, 2: up to 32).
+template <int NCB, bool OUT_BF16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void verify_kernel(VerifyLaunch p) {
+  __shared__ __attribute__((aligned(16))) char s_vt[NW][VT_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int worker = blockIdx.x * NW + wave;
+  const int nworkers = p.num_workers;
+  if (worker >= nworkers) return;
+  const int R = p.num_rows;
+  const int Hq = p.num_q_heads;
+  const int Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int log2G = __builtin_ctz(G);
+  const int lq = lane & 15;                // MFMA row / column index
+  const int lg = lane >> 4;                // MFMA lane group
+  const int tqa = lane & 3;                // V loads: token quad ...
+  const int dg = lane >> 2;                // ... and 8-element group
+  char *vt = s_vt[wave];
+
+  // ---- this worker's share of the flattened (row, kv head, tile) space ----
+  const int *lens = p.seq_lens + p.first_row;
+  long long W = 0;
+  for (int base = 0; base < R; base += 64) {
+    const int r = base + lane;
+    const int n = r < R ? (lens[r] + TILE - 1) / TILE : 0;
+    W += __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), 63);
+  }
+  W *= Hkv;
+  const int nw = (int)min((long long)nworkers, W);
+  if (worker >= nw) return;
+  const long long x0 = (long long)worker * W / nw;
+  const long long x1 = (long long)(worker + 1) * W / nw;
+  auto worker_of = [&](long long x) { return (int)(((x + 1) * nw - 1) / W); };
+
+  int rb = 0;
+  long long rowstart = 0;
+  {
+    long long before = 0;
+    for (int base = 0; base < R; base += 64) {
+      const int r = base + lane;
+      const int n = r < R ? (lens[r] + TILE - 1) / TILE : 0;
+      const int incl = wave_inclusive_scan(n, lane);
+      const long long lo = before + (long long)(incl - n) * Hkv;
+      const long long hi = before + (long long)incl * Hkv;
+      const unsigned long long hit = __builtin_amdgcn_ballot_w64(x0 >= lo && x0 < hi && n > 0);
+      if (hit != 0) {
+        const int k = __builtin_ctzll(hit);
+        rb = base + k;
+        rowstart = readlane64(lo, k);
+        break;
+      }
+      before += (long long)__builtin_amdgcn_readlane(incl, 63) * Hkv;
+    }
+  }
+
+  const int bs = p.block_size;
+  const int log2bs = __builtin_ctz(bs);
+  const size_t page_bytes = (size_t)bs * D * 2;
+  const size_t phys_stride = (size_t)Hkv * page_bytes;
+  const float qk_scale = p.scale * kLog2e;
+
+  int L = lens[rb];
+  int nb = (L + TILE - 1) / TILE;
+  int g = (int)((x0 - rowstart) / nb);
+  int t0 = (int)((x0 - rowstart) % nb);
+  long long ustart = rowstart + (long long)g * nb;
+  long long x = x0;
+
+  while (x < x1) {
+    const int cnt = (int)min((long long)(nb - t0), x1 - x);
+    const int u = rb * Hkv + g;
+    const int row = p.first_row + rb;
+    if (t0 == 0 && lane == 0) {
+      p.seg_first[u] = worker;
+      p.seg_count[u] = worker_of(ustart + nb - 1) - worker + 1;
+    }
+    const bool whole = t0 == 0 && cnt == nb;
+    const int qbase = p.q_start_loc[row];
+    const int n = p.q_start_loc[row + 1] - qbase;
+    const int ncols = n << log2G;
+    const int tok_begin = t0 * TILE;
+    const int tok_end = min((t0 + cnt) * TILE, L);
+    const int first_page = tok_begin >> log2bs;
+    const int last_page = (tok_end - 1) >> log2bs;
+    const int32_t *trow = p.block_table + (size_t)row * p.max_blocks_per_seq;
+    const int mb_last = p.max_blocks_per_seq - 1;
+    int chunk_base = first_page;
+    int tbl = 0;
+
+    // query columns of this lane: Q^T as the B operand, and the last visible position
+    u32x4 qb[NCB][4];
+    int lim[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = 16 * cb + lq;
+      const int qi = c >> log2G;
+      lim[cb] = c < ncols ? L - n + qi : L - 1;
+      const __bf16 *qp = static_cast<const __bf16 *>(p.q) +
+                         ((size_t)(qbase + qi) * Hq + g * G + (c & (G - 1))) * D + 8 * lg;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qb[cb][kk] = c < ncols ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const int mask_from = L - n;           // tiles reaching past this position need the mask
+    const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
+    const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
+
+    // o: O^T blocks; ls: the denominators, accumulated by the same MFMA as O^T from a
+    // V^T row of ones (row 0 of the block: lanes 0..15, element 0), so that numerator and
+    // denominator see the same rounding (a constant V comes out exact)
+    float m[NCB];
+    f32x4 o[8][NCB], ls[NCB];
+    const uint32_t one = lq == 0 ? 0x3F803F80u : 0u;      // bf16 pairs (1, 1): row 0, every k
+    const u32x4 ones = {one, one, one, one};
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      m[cb] = kNegBig;
+      ls[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // K[tb][kk]: token ts + 16 tb + lq, elements 32 kk + 8 lg .. +8 (the MFMA A operand)
+    // V[tb][i]:  token ts + 16 tb + 4 tqa + i, elements 8 dg .. +8
+    auto load_tile = [&](int t, u32x4 (&k)[2][4], u32x4 (&v)[2][4]) {
+      const int ts = tok_begin + t * TILE;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int tok0 = ts + 16 * tb;     // 16 tokens inside one page (bs >= 16)
+        const int page = min(tok0 >> log2bs, last_page);
+        const int phys = __builtin_amdgcn_readlane(tbl, page - chunk_base);
+        const char *kp = kpool + (size_t)phys * phys_stride;
+        const char *vp = vpool + (size_t)phys * phys_stride;
+        const uint32_t koff = (uint32_t)(((tok0 + lq) & (bs - 1)) * (D * 2) + 16 * lg);
+        const uint32_t voff = (uint32_t)(((tok0 + 4 * tqa) & (bs - 1)) * (D * 2) + 16 * dg);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          k[tb][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + koff + 64 * kk));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[tb][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + voff + (D * 2) * i));
+      }
+    };
+
+    auto compute_tile = [&](int t, const u32x4 (&k)[2][4], u32x4 (&v)[2][4]) {
+      const int ts = tok_begin + t * TILE;
+      // ---- V^T into this wave's LDS tile (after the previous tile's operand reads) ----
+      if (ts + TILE > L) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (ts + 16 * tb + 4 * tqa + i >= L) v[tb][i] = u32x4{0u, 0u, 0u, 0u};
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const u32x4 grp = {__builtin_amdgcn_perm(v[0][1][w], v[0][0][w], sel),
+                           __builtin_amdgcn_perm(v[0][3][w], v[0][2][w], sel),
+                           __builtin_amdgcn_perm(v[1][1][w], v[1][0][w], sel),
+                           __builtin_amdgcn_perm(v[1][3][w], v[1][2][w], sel)};
+        *reinterpret_cast<u32x4 *>(vt + vt_offset(8 * dg + e, tqa)) = grp;
+      }
+      // ---- S^T = K Q^T ----
+      f32x4 s[2][NCB];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) s[tb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) s[tb][cb] = mfma(k[tb][kk], qb[cb][kk], s[tb][cb]);
+      // ---- scale, mask, online softmax per column ----
+      const bool masked = ts + TILE - 1 > mask_from;
+      float tmax[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float xv = s[tb][cb][i] * qk_scale;
+            if (masked) xv = ts + 16 * tb + 4 * lg + i <= lim[cb] ? xv : -__builtin_inff();
+            s[tb][cb][i] = xv;
+            mx = fmaxf(mx, xv);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        tmax[cb] = mx;
+      }
+      bool need = false;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) need |= tmax[cb] > m[cb] + kSlack;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const float mn = fmaxf(m[cb], tmax[cb]);
+          const float a = fast_exp2(m[cb] - mn);
+          m[cb] = mn;
+          ls[cb] *= a;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) o[db][cb] *= a;
+        }
+      }
+      u32x4 pb[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = fast_exp2(s[0][cb][i] - m[cb]);
+          pv[4 + i] = fast_exp2(s[1][cb][i] - m[cb]);
+        }
+        pb[cb] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                       pack_bf16(pv[6], pv[7])};
+        ls[cb] = mfma(ones, pb[cb], ls[cb]);
+      }
+      // ---- O^T += V^T P^T ----
+      wave_lds_fence();
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(vt + vt_offset(16 * db + lq, lg));
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[db][cb] = mfma(a, pb[cb], o[db][cb]);
+      }
+    };
+
+    // software pipeline over tiles [ta, tb): three register sets, two tiles in flight
+    // (indices past the last tile are clamped to it so every step issues the same loads)
+    auto run_tiles = [&](int ta, int tb) {
+      const int tl = tb - 1;
+      u32x4 ka[2][4], va[2][4], kb2[2][4], vb2[2][4], kc[2][4], vc[2][4];
+      load_tile(ta, ka, va);
+      load_tile(min(ta + 1, tl), kb2, vb2);
+      for (int t = ta; t < tb; t += 3) {
+        load_tile(min(t + 2, tl), kc, vc);
+        compute_tile(t, ka, va);
+        load_tile(min(t + 3, tl), ka, va);
+        if (t + 1 < tb) compute_tile(t + 1, kb2, vb2);
+        load_tile(min(t + 4, tl), kb2, vb2);
+        if (t + 2 < tb) compute_tile(t + 2, kc, vc);
+      }
+    };
+    // chunks of 64 pages share one block-table load (64 * bs tokens: whole tiles)
+    for (int ta = 0; ta < cnt;) {
+      const int tb = min(cnt, (((chunk_base + 64) << log2bs) - tok_begin) / TILE);
+      tbl = trow[min(chunk_base + lane, mb_last)];
+      run_tiles(ta, tb);
+      ta = tb;
+      chunk_base += 64;
+    }
+
+    // ---- denominators: row 0 of the ones product, held by lanes 0..15; write ----
+    float lsum[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) lsum[cb] = __shfl(ls[cb][0], lq);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = 16 * cb + lq;
+      if (c >= ncols) continue;
+      if (whole) {
+        const size_t base = ((size_t)(qbase + (c >> log2G)) * Hq + g * G + (c & (G - 1))) * D;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const f32x4 v = o[db][cb];
+          const float l = lsum[cb];
+          store4<OUT_BF16>(p.out, base + 16 * db + 4 * lg, f32x4{v[0] / l, v[1] / l, v[2] / l, v[3] / l});
+        }
+      } else {
+        const size_t slot = (size_t)(u + worker) * p.slot_cols + c;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *reinterpret_cast<f32x4 *>(p.part_acc + slot * D + 16 * db + 4 * lg) = o[db][cb];
+        if (lg == 0) {
+          p.part_m[slot] = m[cb];
+          p.part_l[slot] = lsum[cb];
+        }
+      }
+    }
+
+    // next unit
+    x += cnt;
+    t0 = 0;
+    ustart += nb;
+    if (++g == Hkv) {
+      g = 0;
+      ++rb;
+      if (x < x1) {
+        L = lens[rb];
+        nb = (L + TILE - 1) / TILE;
+      }
+    }
+  }
+}
+
+// Combine the pieces of one (row, kv head, query column) cut across workers.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int Hkv = p.num_kv_heads;
+  const int G = p.num_q_heads / Hkv;
+  const int rb = u / Hkv;
+  const int g = u % Hkv;
+  const int row = p.first_row + rb;
+  const int qbase = p.q_start_loc[row];
+  const int n = p.q_start_loc[row + 1] - qbase;
+  if (c >= n * G) return;
+  const int cnt = p.seg_count[u];
+  if (cnt <= 1) return;                    // written directly by its only worker
+  const int first = p.seg_first[u];
+  float M = kNegBig;
+  for (int i = 0; i < cnt; ++i) M = fmaxf(M, p.part_m[(size_t)(u + first + i) * p.slot_cols + c]);
+  float n0 = 0.f, n1 = 0.f, den = 0.f;
+  for (int i = 0; i < cnt; ++i) {
+    const size_t slot = (size_t)(u + first + i) * p.slot_cols + c;
+    const float wt = fast_exp2(p.part_m[slot] - M);
+    den = __builtin_fmaf(wt, p.part_l[slot], den);
+    const float2 a = *reinterpret_cast<const float2 *>(p.part_acc + slot * D + 2 * lane);
+    n0 = __builtin_fmaf(wt, a.x, n0);
+    n1 = __builtin_fmaf(wt, a.y, n1);
+  }
+  const size_t o = ((size_t)(qbase + c / G) * p.num_q_heads + g * G + c % G) * D + 2 * lane;
+  if constexpr (OUT_BF16) {
+    static_cast<__bf16 *>(p.out)[o] = (__bf16)(n0 / den);
+    static_cast<__bf16 *>(p.out)[o + 1] = (__bf16)(n1 / den);
+  } else {
+    static_cast<float *>(p.out)[o] = n0 / den;
+    static_cast<float *>(p.out)[o + 1] = n1 / den;
+  }
+}
+
+template <int NCB>
+int launch_ncb(const VerifyLaunch &V, hipStream_t st) {
+  dim3 grid((V.num_workers + NW - 1) / NW);
+  if (V.out_dtype == PA_BF16)
+    hipLaunchKernelGGL((verify_kernel<NCB, true>), grid, dim3(NT), 0, st, V);
+  else
+    hipLaunchKernelGGL((verify_kernel<NCB, false>), grid, dim3(NT), 0, st, V);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_verify_partials(const VerifyLaunch &V, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return V.slot_cols <= 16 ? launch_ncb<1>(V, st) : launch_ncb<2>(V, st);
+}
+
+int launch_verify_merge(const VerifyLaunch &V, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  dim3 grid(V.slot_cols, V.num_rows * V.num_kv_heads);
+  if (V.out_dtype == PA_BF16)
+    hipLaunchKernelGGL(verify_merge_kernel<true>, grid, dim3(64), 0, st, V);
+  else
+    hipLaunchKernelGGL(verify_merge_kernel<false>, grid, dim3(64), 0, st, V);
+  return (int)hipGetLastError();
+}
+
+}  // namespace pa

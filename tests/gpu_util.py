@@ -20,17 +20,21 @@ def run_decode(w, out_dtype=None, num_workers=0, dev=None):
     return out.float().cpu().numpy().astype(np.float64)
 
 
-def run_mixed(w, out_dtype=None, num_workers=0, dev=None):
+def run_mixed(w, out_dtype=None, num_workers=0, dev=None, num_verify_rows=0):
+    """pa_mixed on a workload: rows [0, nd) decode, the next num_verify_rows verify rows, then prefill."""
     import torch
     from paged_kv_attention_13_amd import binding
     from paged_kv_attention_13_amd.device import to_device
     d = dev or to_device(w)
     odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
-    prefill_q = w.q_lens[w.num_decode_rows:]
+    nd, nv = w.num_decode_rows, num_verify_rows
+    verify_q = w.q_lens[nd:nd + nv]
+    prefill_q = w.q_lens[nd + nv:]
     out = binding.mixed(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
-                        d["q_start_loc"], w.scale, num_decode_rows=w.num_decode_rows,
+                        d["q_start_loc"], w.scale, num_decode_rows=nd,
                         max_q_len=int(prefill_q.max()) if len(prefill_q) else 1,
-                        max_seq_len=w.max_seq_len, out_dtype=odt, num_workers=num_workers)
+                        max_seq_len=w.max_seq_len, out_dtype=odt, num_workers=num_workers,
+                        num_verify_rows=nv, max_verify_q_len=int(verify_q.max()) if nv else 0)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(b):
 
 
 def test_abi_version(b):
-    assert b.LIB.pa_abi_version() == 1
+    assert b.LIB.pa_abi_version() == 2
 
 
 def test_struct_layout_matches_header(b):
@@ -51,6 +51,10 @@ def test_struct_layout_matches_header(b):
     assert b.DecodeArgs.scale.offset == 48 + 7 * 8
     assert ctypes.sizeof(b.DecodeArgs) == 48 + 7 * 8 + 8 + 3 * 8
     assert b.MixedArgs.q_start_loc.offset == ctypes.sizeof(b.DecodeArgs)
+    nb = ctypes.sizeof(b.DecodeArgs)
+    assert b.MixedArgs.num_verify_rows.offset == nb + 8 + 3 * 4
+    assert b.MixedArgs.max_verify_q_len.offset == nb + 8 + 4 * 4
+    assert ctypes.sizeof(b.MixedArgs) == nb + 8 + 5 * 4 + 4      # padded to 8 bytes
 
 
 def _args(b, **kw):
@@ -148,6 +152,83 @@ def test_mixed_validation(b):
     assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_NULL_POINTER"
 
 
+def _mixed_args(b, **kw):
+    m = b.MixedArgs()
+    m.base = _args(b, num_seqs=4, max_seq_len=128)
+    m.q_start_loc = 0x10000
+    m.total_q = 12
+    m.num_decode_rows = 1
+    m.num_verify_rows = 2
+    m.max_verify_q_len = 4
+    m.max_q_len = 8
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_verify_rows=4), "PA_ERR_BAD_SHAPE"),            # 1 decode + 4 verify > 4 rows
+    (dict(num_verify_rows=-1), "PA_ERR_BAD_SHAPE"),
+    (dict(max_verify_q_len=0), "PA_ERR_UNSUPPORTED"),
+    (dict(max_verify_q_len=9), "PA_ERR_UNSUPPORTED"),          # 9 x group 4 > 32 columns
+    (dict(total_q=3), "PA_ERR_BAD_SHAPE"),
+])
+def test_mixed_verify_class_validation(b, kw, status):
+    m = _mixed_args(b, **kw)
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == status
+
+
+def test_mixed_verify_rows_need_bf16_kv(b):
+    m = _mixed_args(b, num_decode_rows=2, num_verify_rows=2)   # no prefill rows
+    m.base.kv_dtype = b.PA_FP8_E4M3
+    m.base.k_scale = m.base.v_scale = 0x10000
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
+    m.num_verify_rows = 0
+    m.num_decode_rows = 4                                      # FP8 decode rows alone are fine
+    n = ctypes.c_size_t()
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+
+
+def test_mixed_group_bounds_verify_q_len(b):
+    # group 8: at most 4 queries per verify row; group 1: up to 32
+    m = _mixed_args(b, max_verify_q_len=5)
+    m.base.num_q_heads = 64
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
+    m.max_verify_q_len = 4
+    n = ctypes.c_size_t()
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    m.base.num_q_heads = 8
+    m.max_verify_q_len = 32
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    m.max_verify_q_len = 33
+    assert b.STATUS_NAMES[b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n))] == \
+        "PA_ERR_UNSUPPORTED"
+
+
+def test_mixed_workspace_holds_verify_partials(b):
+    """Workspace = decode part (rounded to 256 B) + verify records and partial slots."""
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    m = _mixed_args(b, num_verify_rows=0)
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n0)) == 0
+    m = _mixed_args(b)
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n1)) == 0
+    r256 = lambda x: (x + 255) // 256 * 256
+    units = 2 * 8                                             # verify rows x kv heads
+    workers = min(1024, max(1, (units * 4 + 3) // 4))         # max_seq_len 128 = 4 tiles of 32
+    slots = (units + workers) * 4 * 4                         # max_verify_q_len 4 x group 4
+    vbytes = r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 128 * 4)
+    assert n1.value == r256(n0.value) + vbytes
+    # an explicit worker count applies to the verify rows too
+    m.base.num_workers = 3
+    n2 = ctypes.c_size_t()
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n2)) == 0
+    m.num_verify_rows = 0
+    n3 = ctypes.c_size_t()
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n3)) == 0
+    slots = (units + 3) * 16
+    assert n2.value == r256(n3.value) + r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 512)
+
+
 def _meta(b, table, lens, **kw):
     args = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=10,
                 max_seq_len=64)
@@ -178,6 +259,15 @@ def test_mixed_metadata_checker(b):
         b.check_mixed_metadata(table, [5, 20, 40], [0, 1, 30, 49], num_decode_rows=1, max_q_len=40, **kw)
     with pytest.raises(b.PagedAttentionError, match="max_q_len"):
         b.check_mixed_metadata(table, [5, 20, 40], [0, 1, 9, 49], num_decode_rows=1, max_q_len=30, **kw)
+    # row 1 as a verify row (q_len 8)
+    b.check_mixed_metadata(table, [5, 20, 40], [0, 1, 9, 49], num_decode_rows=1, max_q_len=40,
+                           num_verify_rows=1, max_verify_q_len=8, **kw)
+    with pytest.raises(b.PagedAttentionError, match="max_verify_q_len"):
+        b.check_mixed_metadata(table, [5, 20, 40], [0, 1, 9, 49], num_decode_rows=1, max_q_len=40,
+                               num_verify_rows=1, max_verify_q_len=7, **kw)
+    with pytest.raises(b.PagedAttentionError, match="do not fit"):
+        b.check_mixed_metadata(table, [5, 20, 40], [0, 1, 9, 49], num_decode_rows=1, max_q_len=40,
+                               num_verify_rows=3, max_verify_q_len=8, **kw)
 
 
 def test_status_strings(b):

@@ -75,7 +75,7 @@ def test_generator_is_deterministic_and_shaped():
     assert len(set(used.tolist())) == len(used)                          # no two rows share a block
 
 
-@pytest.mark.parametrize("i", [1, 2, 4, 5])
+@pytest.mark.parametrize("i", [1, 2, 4, 5, 6])
 def test_named_workload_lengths(i):
     L, ql = pa_inputs.workload_lengths(i)
     if i == 1:
@@ -90,6 +90,8 @@ def test_named_workload_lengths(i):
         assert len(L) == 104 and np.all(ql[:96] == 1) and np.all(ql[96:] == 256)
         assert L[:96].min() >= 256 and L[:96].max() <= 8192
         assert np.all(L[96:] >= 256) and np.all(L[96:] <= 2048 + 256)
+    if i == 6:
+        assert len(L) == 55 and np.all(L == 8192) and np.all(ql == 4)
 
 
 def test_fp8_quantiser_roundtrip_bound():
