@@ -42,10 +42,11 @@ def parse():
                     help="decode work split into this many waves (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "append-fp8"],
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "append-fp8", "cascade"],
                     help="decode: the attention call of --workload (default); append / append-fp8: "
                          "writing the mixed workload's 2,144 new tokens (96 decode + 8 x 256 prefill) "
-                         "into their cache slots, bf16 -> bf16 or bf16 -> FP8-E4M3")
+                         "into their cache slots, bf16 -> bf16 or bf16 -> FP8-E4M3; cascade: the "
+                         "shared-prefix decode call on workload 7, with pa_decode on the same rows beside it")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed loop, run one device-to-device copy of this many MiB "
                          "(a plain copy kernel of known size, to calibrate HBM byte counters)")
@@ -183,6 +184,81 @@ def bench_append(args):
     }), flush=True)
 
 
+def _timed(call, steps, warmup):
+    """Mean ms per call from events around each call, and wall ms per call over the loop."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return float(np.mean([e[0].elapsed_time(e[1]) for e in evs])), wall
+
+
+def bench_cascade(args):
+    """Shared-prefix decode (workload 7): pa_decode_cascade, and pa_decode on the same rows."""
+    import numpy as np
+    import torch
+
+    import pa_inputs
+    from paged_kv_attention_13_amd import accounting, binding
+    from paged_kv_attention_13_amd.device import to_device
+
+    w = pa_inputs.make_config(7)
+    d = to_device(w)
+    out = torch.empty(d["q"].shape, dtype=torch.bfloat16, device="cuda")
+    rows_per_group = int(np.diff(w.group_start).max())
+    c = binding.make_cascade_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                  d["group_start"], d["shared_len"], w.scale, max_seq_len=w.max_seq_len,
+                                  max_group_rows=rows_per_group, out=out, num_workers=args.num_workers)
+    ws = torch.empty(max(binding.cascade_workspace_bytes(c), 16), dtype=torch.uint8, device="cuda")
+    c.base.workspace, c.base.workspace_bytes = ws.data_ptr(), ws.numel()
+    a = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], w.scale,
+                                 max_seq_len=w.max_seq_len, out=torch.empty_like(out),
+                                 num_workers=args.num_workers)
+    wsd = torch.empty(max(binding.plan(a).workspace_bytes, 16), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = wsd.data_ptr(), wsd.numel()
+
+    c_ms, c_wall = _timed(lambda: binding.cascade_args_call(c), args.steps, args.warmup)
+    d_ms, d_wall = _timed(lambda: binding.decode_args_call(a), args.steps, args.warmup)
+
+    Hkv, D = w.num_kv_heads, w.head_dim
+    logical = accounting.kv_bytes(w.seq_lens, Hkv, D, "bf16")             # every row's whole cache
+    gs = w.group_start
+    shared = [int(w.shared_len[gs[k]]) for k in range(len(gs) - 1)]
+    own = accounting.kv_bytes(w.seq_lens - w.shared_len, Hkv, D, "bf16")
+    physical = own + accounting.kv_bytes(np.array(shared), Hkv, D, "bf16")  # each prefix once per group
+    q_bytes = int(w.q.nbytes)
+    ach = (physical + q_bytes) / (c_ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "shared-prefix decode: effective KV GB/s (every row's whole cache / step time)",
+        "value": round(logical / (c_wall * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(c_wall, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values; 64 rows sharing the blocks of one 1,488-token prefix)",
+        "config": {"workload": w.name, "batch": w.num_seqs, "groups": len(gs) - 1,
+                   "shared_tokens": shared[0], "context_tokens": int(w.seq_lens.sum()),
+                   "block_size": w.block_size, "q_heads": w.num_q_heads, "kv_heads": Hkv, "head_dim": D},
+        "logical_kv_bytes": int(logical), "physical_kv_bytes": int(physical),
+        "cascade_call_ms": round(c_ms, 5),
+        "decode_same_rows": {"call_ms": round(d_ms, 5), "ms_per_step": round(d_wall, 5),
+                             "effective_GBs": round(logical / (d_wall * 1e-3) / 1e9, 1)},
+        "speedup_vs_decode": round(d_wall / c_wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode_cascade call (prefix + row-part + merge kernels)",
+                     "kernel_ms_mean": round(c_ms, 5), "bytes_per_launch": int(physical + q_bytes)},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -191,6 +267,9 @@ def main():
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
+    if args.op == "cascade":
+        bench_cascade(args)
+        return
     if args.op != "decode":
         bench_append(args)
         return

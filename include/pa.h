@@ -167,6 +167,34 @@ typedef struct pa_append_args {
   const float *v_scale;        /* [Hkv], same rule */
 } pa_append_args;
 
+/* Arguments of a shared-prefix (cascade) decode call.  Rows that begin with the
+ * same tokens can point at the same cache blocks (prefix reuse: "How does
+ * TensorRT-LLM work" (outcomeschool.com), section "The paged KV cache"; block
+ * reuse for a shared system prompt: "TensorRT-LLM, in depth" (aicassindra.com),
+ * section "The paged KV cache and block reuse").  Consecutive decode rows are
+ * grouped; the rows of a group share the first shared_len tokens of their
+ * caches, held in the same physical blocks.  The call reads each shared block
+ * once per group: the group's queries (up to 32 query columns per kv head) are
+ * attended over the shared prefix together, each row over the rest of its own
+ * cache, and the two parts are combined with the log-sum-exp identity.  The
+ * result is the same attention pa_decode computes; only the bytes read differ.
+ * bf16 q and KV. */
+typedef struct pa_cascade_args {
+  pa_decode_args base;         /* the decode rows; base.num_workers (if nonzero) sets the
+                                  work split of both kernels */
+  const int32_t *group_start;  /* [num_groups + 1]: group k is rows [group_start[k],
+                                  group_start[k + 1]); group_start[0] = 0, strictly
+                                  increasing, group_start[num_groups] = num_seqs */
+  const int32_t *shared_len;   /* [num_seqs]: tokens of the row's cache its group shares:
+                                  equal within a group, a multiple of block_size,
+                                  0 <= shared_len < seq_len, and the first
+                                  shared_len / block_size block-table entries equal
+                                  across the group */
+  int32_t num_groups;          /* >= 1 when num_seqs > 0 */
+  int32_t max_group_rows;      /* host-known bound on rows per group; with G = Hq/Hkv,
+                                  max_group_rows * G <= 32 (split larger groups) */
+} pa_cascade_args;
+
 /* Launch plan of a decode call. */
 typedef struct pa_plan {
   int32_t num_workers;         /* worker waves the decode kernel runs */
@@ -210,6 +238,15 @@ pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
  * on `stream`.  The workspace (pa_mixed_workspace_size) holds the decode rows'
  * split records and partials followed by the verify rows'. */
 pa_status pa_mixed(const pa_mixed_args *a, void *stream);
+
+/* Shared-prefix decode: the prefix kernel (one pass over each group's shared
+ * blocks), the decode kernel over each row's own tokens, then the merge, all on
+ * `stream`.  Workspace: pa_cascade_workspace_size.  The device-resident group
+ * arrays are preconditions like the block table; pa_check_cascade_metadata
+ * verifies them (and the decode preconditions) on host copies. */
+pa_status pa_cascade_workspace_size(const pa_cascade_args *a, size_t *bytes);
+pa_status pa_decode_cascade(const pa_cascade_args *a, void *stream);
+pa_status pa_check_cascade_metadata(const pa_cascade_args *a_host);
 
 /* Append: copy (or quantise) each token's [Hkv][D] K and V rows into
  * pool[slot / bs][:, slot % bs, :].  Precondition: -1 <= slot_mapping[t] <

@@ -59,6 +59,8 @@ class Workload:
     v_scale: Optional[np.ndarray] = None
     scale: float = 0.0             # softmax scale; 1/sqrt(D) unless stated
     num_decode_rows: int = 0
+    group_start: Optional[np.ndarray] = None   # int32 [groups + 1]: rows sharing a cache prefix
+    shared_len: Optional[np.ndarray] = None    # int32 [B]: tokens of the row's cache its group shares
 
     @property
     def num_seqs(self) -> int:
@@ -237,6 +239,80 @@ def make_workload(*, name: str, seq_lens, q_lens=None, num_q_heads=32, num_kv_he
     return w
 
 
+def make_shared_prefix_workload(*, name: str, group_sizes, shared_lens, own_lens, prefix_ids=None,
+                                num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                                extra_blocks: int = 0, seed: int = 0,
+                                poison_unused: bool = False) -> Workload:
+    """Decode rows in groups whose caches start with the same blocks.
+
+    Group k has ``group_sizes[k]`` consecutive rows whose first ``shared_lens[k]``
+    tokens (a multiple of ``block_size``) live in the same physical blocks;
+    groups with equal ``prefix_ids`` share the same prefix blocks too (one
+    system prompt for many groups).  Row b then has ``own_lens[b] >= 1`` tokens
+    of its own in blocks no other row uses, so ``seq_len = shared + own``.
+    Physical blocks come from a seeded random permutation of the pool.
+    """
+    group_sizes = [int(n) for n in group_sizes]
+    shared_lens = [int(p) for p in shared_lens]
+    own_lens = np.asarray(own_lens, dtype=np.int64)
+    prefix_ids = list(range(len(group_sizes))) if prefix_ids is None else [int(i) for i in prefix_ids]
+    if any(p % block_size for p in shared_lens) or np.any(own_lens < 1):
+        raise ValueError("shared lengths must be whole blocks and every row needs own tokens")
+    B = sum(group_sizes)
+    if len(own_lens) != B:
+        raise ValueError("own_lens needs one entry per row")
+    ss_table, ss_q, ss_k, ss_v = np.random.SeedSequence(seed).spawn(4)
+    rng = np.random.default_rng(ss_table)
+    shared_of_row = np.repeat(np.asarray(shared_lens, dtype=np.int64), group_sizes)
+    seq_lens = (shared_of_row + own_lens).astype(np.int32)
+    prefix_blocks = {}
+    for pid, p in zip(prefix_ids, shared_lens):
+        prefix_blocks[pid] = max(prefix_blocks.get(pid, 0), p // block_size)
+    own_blocks = (shared_of_row % block_size + own_lens + block_size - 1) // block_size
+    need = sum(prefix_blocks.values()) + int(own_blocks.sum())
+    num_blocks = need + int(extra_blocks)
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    pos = 0
+    prefix_phys = {}
+    for pid in sorted(prefix_blocks):
+        prefix_phys[pid] = perm[pos:pos + prefix_blocks[pid]]
+        pos += prefix_blocks[pid]
+    mb = int(blocks_needed(seq_lens, block_size).max())
+    table = np.full((B, mb), -1, dtype=np.int32)
+    group_start = np.zeros(len(group_sizes) + 1, dtype=np.int32)
+    np.cumsum(group_sizes, out=group_start[1:])
+    b = 0
+    for k, n in enumerate(group_sizes):
+        nshared = shared_lens[k] // block_size
+        for _ in range(n):
+            table[b, :nshared] = prefix_phys[prefix_ids[k]][:nshared]
+            table[b, nshared:nshared + own_blocks[b]] = perm[pos:pos + own_blocks[b]]
+            pos += int(own_blocks[b])
+            b += 1
+    q = _store(_normal(ss_q, (B, num_q_heads, head_dim)), "bf16")
+    kshape = (num_blocks, num_kv_heads, block_size, head_dim)
+    k_pool = _store(_normal(ss_k, kshape), "bf16")
+    v_pool = _store(_normal(ss_v, kshape), "bf16")
+    w = Workload(name=name, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                 block_size=block_size, q_fmt="bf16", kv_fmt="bf16", q=q, k_pool=k_pool, v_pool=v_pool,
+                 block_table=table, seq_lens=seq_lens, q_lens=np.ones(B, np.int32),
+                 scale=1.0 / np.sqrt(head_dim), num_decode_rows=B, group_start=group_start,
+                 shared_len=shared_of_row.astype(np.int32))
+    if poison_unused:
+        poison_pool(w)
+    return w
+
+
+def split_groups(group_sizes, max_rows: int):
+    """Cut groups larger than ``max_rows`` into consecutive groups of at most ``max_rows`` rows."""
+    out = []
+    for n in group_sizes:
+        while n > 0:
+            out.append(min(n, max_rows))
+            n -= out[-1]
+    return out
+
+
 def leading_decode_rows(q_lens: np.ndarray) -> int:
     """Number of leading rows with q_len == 1 (decode rows come first in a mixed batch)."""
     big = np.nonzero(np.asarray(q_lens) != 1)[0]
@@ -269,6 +345,8 @@ def poison_pool(w: Workload) -> None:
 # the five named workloads
 # ----------------------------------------------------------------------------
 
+SHARED_PROMPT_7 = 1488      # whole 16-token blocks of workload 7's 1,500-token system prompt
+
 WORKLOAD_NAMES = {
     1: "decode fp32 B1 ctx512 bs16",
     2: "decode bf16 B32 ctxU[1,4096] bs16 pool2x",
@@ -276,6 +354,7 @@ WORKLOAD_NAMES = {
     4: "decode fp8kv B128 ctxlogU[128,8192] bs16",
     5: "mixed bf16 8x256-chunk prefill + 96 decode bs16",
     6: "verify bf16 B55 ctx8192 q4 bs64",
+    7: "shared-prefix decode bf16 B64 (8 groups of 8) 1488 shared + 312 + U[1,250] bs16",
 }
 
 
@@ -303,11 +382,18 @@ def workload_lengths(i: int, seed: Optional[int] = None):
         # speculative decoding: every row checks 4 drafted tokens in one pass; the long
         # context of workload 3, so its KV bytes equal that workload's
         return np.full(55, 8192, np.int32), np.full(55, 4, np.int32)
+    if i == 7:
+        # the support-assistant example: a 1,500-token system prompt shared by every
+        # conversation (its 93 full 16-token blocks), then per row the prompt's last 12
+        # tokens, a 300-token question and 1..250 tokens generated so far; 64 rows
+        # (max_batch_size) in groups of 8
+        gen = rng.integers(1, 250 + 1, size=64)
+        return (SHARED_PROMPT_7 + 12 + 300 + gen).astype(np.int32), np.ones(64, np.int32)
     raise ValueError(i)
 
 
 def make_config(i: int, seed: Optional[int] = None, poison_unused: bool = False) -> Workload:
-    """Named workload i (1..6) at full size."""
+    """Named workload i (1..7) at full size."""
     seed = (1000 + i) if seed is None else seed
     L, ql = workload_lengths(i, seed)
     common = dict(name=WORKLOAD_NAMES[i], seq_lens=L, q_lens=ql, seed=seed + 7919,
@@ -324,4 +410,9 @@ def make_config(i: int, seed: Optional[int] = None, poison_unused: bool = False)
         return make_workload(block_size=16, **common)
     if i == 6:
         return make_workload(block_size=64, **common)
+    if i == 7:
+        return make_shared_prefix_workload(name=WORKLOAD_NAMES[7], group_sizes=[8] * 8,
+                                           shared_lens=[SHARED_PROMPT_7] * 8, own_lens=L - SHARED_PROMPT_7,
+                                           prefix_ids=[0] * 8, block_size=16, seed=seed + 7919,
+                                           poison_unused=poison_unused)
     raise ValueError(i)

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: 
 
 EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_decode",
             "pa_decode_partials", "pa_merge_partials", "pa_mixed", "pa_append", "pa_check_decode_metadata",
-            "pa_check_mixed_metadata", "pa_check_append_metadata", "pa_status_string", "pa_last_error"]
+            "pa_check_mixed_metadata", "pa_check_append_metadata", "pa_cascade_workspace_size",
+            "pa_decode_cascade", "pa_check_cascade_metadata", "pa_status_string", "pa_last_error"]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -62,6 +63,16 @@ class MixedArgs(ctypes.Structure):
         ("max_q_len", ctypes.c_int32),
         ("num_verify_rows", ctypes.c_int32),
         ("max_verify_q_len", ctypes.c_int32),
+    ]
+
+
+class CascadeArgs(ctypes.Structure):
+    _fields_ = [
+        ("base", DecodeArgs),
+        ("group_start", ctypes.c_void_p),
+        ("shared_len", ctypes.c_void_p),
+        ("num_groups", ctypes.c_int32),
+        ("max_group_rows", ctypes.c_int32),
     ]
 
 
@@ -112,6 +123,9 @@ def _load():
         "pa_check_append_metadata": ([P(AppendArgs)], ctypes.c_int),
         "pa_check_decode_metadata": ([P(DecodeArgs)], ctypes.c_int),
         "pa_check_mixed_metadata": ([P(MixedArgs)], ctypes.c_int),
+        "pa_cascade_workspace_size": ([P(CascadeArgs), P(ctypes.c_size_t)], ctypes.c_int),
+        "pa_decode_cascade": ([P(CascadeArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_check_cascade_metadata": ([P(CascadeArgs)], ctypes.c_int),
         "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "pa_last_error": ([], ctypes.c_char_p),
     }
@@ -328,6 +342,70 @@ def check_mixed_metadata(block_table, seq_lens, q_start_loc, *, num_decode_rows:
     m.num_verify_rows = num_verify_rows
     m.max_verify_q_len = max_verify_q_len
     check(LIB.pa_check_mixed_metadata(ctypes.byref(m)))
+
+
+def make_cascade_args(q, k_pool, v_pool, block_table, seq_lens, group_start, shared_len, scale, *,
+                      max_seq_len: int, max_group_rows: int, out=None, num_workers: int = 0) -> CascadeArgs:
+    c = CascadeArgs()
+    c.base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
+                              out=out, num_workers=num_workers)
+    c.group_start = _ptr(group_start)
+    c.shared_len = _ptr(shared_len)
+    c.num_groups = int(group_start.shape[0]) - 1
+    c.max_group_rows = int(max_group_rows)
+    return c
+
+
+def cascade_workspace_bytes(c: CascadeArgs) -> int:
+    n = ctypes.c_size_t()
+    check(LIB.pa_cascade_workspace_size(ctypes.byref(c), ctypes.byref(n)))
+    return int(n.value)
+
+
+def decode_cascade(q, k_pool, v_pool, block_table, seq_lens, group_start, shared_len, scale, *,
+                   max_seq_len: int, max_group_rows: int, out=None, out_dtype=None, num_workers: int = 0,
+                   workspace=None, stream=None):
+    """Shared-prefix decode (``pa_decode_cascade``).  Returns ``out`` [B, Hq, D]."""
+    if out is None:
+        out = _alloc_out(q, out_dtype)
+    c = make_cascade_args(q, k_pool, v_pool, block_table, seq_lens, group_start, shared_len, scale,
+                          max_seq_len=max_seq_len, max_group_rows=max_group_rows, out=out,
+                          num_workers=num_workers)
+    if workspace is None:
+        workspace = _alloc_workspace(cascade_workspace_bytes(c), q.device)
+    if workspace is not None:
+        c.base.workspace = _ptr(workspace)
+        c.base.workspace_bytes = workspace.numel() * workspace.element_size()
+    check(LIB.pa_decode_cascade(ctypes.byref(c), ctypes.c_void_p(_stream(stream))))
+    return out
+
+
+def cascade_args_call(c: CascadeArgs, stream=None) -> None:
+    check(LIB.pa_decode_cascade(ctypes.byref(c), ctypes.c_void_p(_stream(stream))))
+
+
+def check_cascade_metadata(block_table, seq_lens, group_start, shared_len, *, max_group_rows: int,
+                           num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                           num_blocks: int, max_seq_len: int) -> None:
+    """Host-side precondition check (``pa_check_cascade_metadata``) on numpy int32 arrays."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    gs = np.ascontiguousarray(group_start, dtype=np.int32)
+    sh = np.ascontiguousarray(shared_len, dtype=np.int32)
+    c = CascadeArgs()
+    a = c.base
+    a.num_seqs, a.num_q_heads, a.num_kv_heads = len(sl), num_q_heads, num_kv_heads
+    a.head_dim, a.block_size, a.num_blocks = head_dim, block_size, num_blocks
+    a.max_blocks_per_seq, a.max_seq_len = bt.shape[1], max_seq_len
+    a.q_dtype = a.kv_dtype = a.out_dtype = PA_BF16
+    a.block_table = bt.ctypes.data
+    a.seq_lens = sl.ctypes.data
+    c.group_start = gs.ctypes.data
+    c.shared_len = sh.ctypes.data
+    c.num_groups = len(gs) - 1
+    c.max_group_rows = max_group_rows
+    check(LIB.pa_check_cascade_metadata(ctypes.byref(c)))
 
 
 def make_append_args(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None) -> AppendArgs:

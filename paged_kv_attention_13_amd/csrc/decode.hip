@@ -124,7 +124,9 @@ __device__ __forceinline__ long long readlane64(long long v, int k) {
   return ((long long)hi << 32) | (unsigned int)lo;
 }
 
-template <int KV, int G, bool OUT_BF16>
+// CASCADE: each row covers only its tokens from kv_start[b] on (the rest of its cache
+// is a shared prefix handled elsewhere), and every piece is left as a partial.
+template <int KV, int G, bool OUT_BF16, bool CASCADE>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   constexpr int EB = KvTraits<KV>::EB;
   constexpr int TPL = KvTraits<KV>::TPL;   // tokens per lane per tile
@@ -143,13 +145,24 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   const int Hkv = p.num_kv_heads;
   const int c = lane & 7;                  // element slot inside the token row
   const int grp = lane >> 3;               // token group 0..7
+  // tokens of row r this kernel covers
+  auto span_of = [&](int r) -> int {
+    if constexpr (CASCADE) return p.seq_lens[r] - p.kv_start[r];
+    else return p.seq_lens[r];
+  };
 
   // ---- this worker's share of the flattened (row, kv head, tile) space ----
   long long W = 0;
+  int n_first = 0, incl_first = 0;         // the first 64 rows' counts, kept for the search below
   for (int base = 0; base < B; base += 64) {
     const int r = base + lane;
-    const int n = r < B ? (p.seq_lens[r] + TILE - 1) / TILE : 0;
-    W += __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), 63);
+    const int n = r < B ? (span_of(r) + TILE - 1) / TILE : 0;
+    const int incl = wave_inclusive_scan(n, lane);
+    if (base == 0) {
+      n_first = n;
+      incl_first = incl;
+    }
+    W += __builtin_amdgcn_readlane(incl, 63);
   }
   W *= Hkv;
   // Planned launches hold two waves per SIMD.  With long work per wave one wave per SIMD
@@ -158,6 +171,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   // workgroups, one per CU, the rest exit at once.
   int nwk = nworkers;
   if (p.workers_auto && (nwk % (2 * NW * kTargetCUs)) == 0 && W >= 128LL * (nwk / 2)) nwk /= 2;
+  // the plan sized the launch for rows of max_seq_len; shorter rows get fewer, longer ranges
+  if (p.workers_auto) nwk = (int)min((long long)nwk, max(1LL, W / p.min_tiles));
   // never more workers than tiles, so that every worker's range is non-empty and the
   // workers covering a unit are exactly the consecutive ones from its first to its last
   const int nw = (int)min((long long)nwk, W);
@@ -174,8 +189,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
     long long before = 0;
     for (int base = 0; base < B; base += 64) {
       const int r = base + lane;
-      const int n = r < B ? (p.seq_lens[r] + TILE - 1) / TILE : 0;
-      const int incl = wave_inclusive_scan(n, lane);
+      const int n = base == 0 ? n_first : (r < B ? (span_of(r) + TILE - 1) / TILE : 0);
+      const int incl = base == 0 ? incl_first : wave_inclusive_scan(n, lane);
       const long long lo = before + (long long)(incl - n) * Hkv;
       const long long hi = before + (long long)incl * Hkv;
       const unsigned long long hit = __builtin_amdgcn_ballot_w64(x0 >= lo && x0 < hi && n > 0);
@@ -195,7 +210,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   const size_t phys_stride = (size_t)Hkv * page_bytes;
   const int lane_off = c * 16;
 
-  int L = p.seq_lens[b];
+  int L = span_of(b);
   int nb = (L + TILE - 1) / TILE;
   int g = (int)((x0 - rowstart) / nb);
   int t0 = (int)((x0 - rowstart) % nb);
@@ -209,15 +224,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
       p.seg_first[u] = worker;
       p.seg_count[u] = worker_of(ustart + nb - 1) - worker + 1;
     }
-    const bool whole = t0 == 0 && cnt == nb;
+    const bool whole = !CASCADE && t0 == 0 && cnt == nb;
     const int tok_begin = t0 * TILE;
     const int tok_end = min((t0 + cnt) * TILE, L);
     const int first_page = tok_begin >> log2bs;
     const int last_page = (tok_end - 1) >> log2bs;
 
     // block-table entries, one per lane, for a chunk of up to 64 pages
-    const int32_t *trow = p.block_table + (size_t)b * p.max_blocks_per_seq;
-    const int mb_last = p.max_blocks_per_seq - 1;
+    const int skip_pages = CASCADE ? (p.kv_start[b] >> log2bs) : 0;
+    const int32_t *trow = p.block_table + (size_t)b * p.max_blocks_per_seq + skip_pages;
+    const int mb_last = p.max_blocks_per_seq - 1 - skip_pages;
     int chunk_base = first_page;
     int tbl = 0;
 
@@ -521,7 +537,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
       g = 0;
       ++b;
       if (x < x1) {
-        L = p.seq_lens[b];
+        L = span_of(b);
         nb = (L + TILE - 1) / TILE;
       }
     }
@@ -561,10 +577,19 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch p) {
 template <int KV, int G>
 int launch_kv_g(const DecodeLaunch &L, hipStream_t st) {
   dim3 grid((L.num_workers + NW - 1) / NW);
+  if constexpr (KV == PA_BF16) {
+    if (L.kv_start) {
+      if (L.out_dtype == PA_BF16)
+        hipLaunchKernelGGL((decode_kernel<KV, G, true, true>), grid, dim3(NT), 0, st, L);
+      else
+        hipLaunchKernelGGL((decode_kernel<KV, G, false, true>), grid, dim3(NT), 0, st, L);
+      return (int)hipGetLastError();
+    }
+  }
   if (L.out_dtype == PA_BF16)
-    hipLaunchKernelGGL((decode_kernel<KV, G, true>), grid, dim3(NT), 0, st, L);
+    hipLaunchKernelGGL((decode_kernel<KV, G, true, false>), grid, dim3(NT), 0, st, L);
   else
-    hipLaunchKernelGGL((decode_kernel<KV, G, false>), grid, dim3(NT), 0, st, L);
+    hipLaunchKernelGGL((decode_kernel<KV, G, false, false>), grid, dim3(NT), 0, st, L);
   return (int)hipGetLastError();
 }
 

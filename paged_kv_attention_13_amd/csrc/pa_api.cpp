@@ -125,4 +125,18 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
   return PA_OK;
 }
 
+pa_status pa_decode_cascade(const pa_cascade_args *a, void *stream) {
+  DecodeLaunch d;
+  VerifyLaunch pre;
+  CascadeMergeLaunch m;
+  size_t total = 0;
+  pa_status s = plan_cascade(a, true, &d, &pre, &m, &total);
+  if (s != PA_OK || a->base.num_seqs == 0) return s;
+  s = hip_status(launch_verify_partials(pre, stream), "shared-prefix");
+  if (s != PA_OK) return s;
+  s = hip_status(launch_decode_partials(d, stream), "decode");
+  if (s != PA_OK) return s;
+  return hip_status(launch_cascade_merge(m, stream), "cascade merge");
+}
+
 }  // extern "C"

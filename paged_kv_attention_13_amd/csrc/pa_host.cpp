@@ -137,6 +137,7 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   L->max_blocks_per_seq = a->max_blocks_per_seq;
   L->num_workers = plan.num_workers;
   L->workers_auto = a->num_workers == 0;
+  L->min_tiles = kMinTilesPerWorker;
   L->kv_dtype = a->kv_dtype;
   L->out_dtype = a->out_dtype;
   L->scale = a->scale;
@@ -237,6 +238,8 @@ pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_
   V->block_size = b.block_size;
   V->max_blocks_per_seq = b.max_blocks_per_seq;
   V->num_workers = workers;
+  V->workers_auto = b.num_workers == 0;
+  V->min_tiles = kMinTilesPerWorker;
   V->slot_cols = a->max_verify_q_len * G;
   V->out_dtype = b.out_dtype;
   V->scale = b.scale;
@@ -251,6 +254,115 @@ pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_
   V->part_l = reinterpret_cast<float *>(base);
   base += round_up(slots * sizeof(float), 256);
   V->part_acc = reinterpret_cast<float *>(base);
+  return PA_OK;
+}
+
+pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, DecodeLaunch *dec,
+                       VerifyLaunch *pre, CascadeMergeLaunch *mrg, size_t *total_bytes) {
+  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  const pa_decode_args &b = a->base;
+  pa_status s = validate_decode(&b, need_device_pointers);
+  if (s != PA_OK) return s;
+  if (b.num_seqs > 0 && (b.q_dtype != PA_BF16 || b.kv_dtype != PA_BF16))
+    return set_error(PA_ERR_UNSUPPORTED, "shared-prefix decode needs bf16 q and a bf16 KV cache");
+  const int B = b.num_seqs;
+  const int G = b.num_q_heads / b.num_kv_heads;
+  if (B > 0 && (a->num_groups < 1 || a->num_groups > B))
+    return set_error(PA_ERR_BAD_SHAPE, "num_groups=%d outside [1, num_seqs=%d]", a->num_groups, B);
+  if (B > 0 && (a->max_group_rows < 1 || (int64_t)a->max_group_rows * G > kVerifyMaxCols))
+    return set_error(PA_ERR_UNSUPPORTED,
+                     "max_group_rows=%d with group size %d: need 1 <= max_group_rows * group <= %d",
+                     a->max_group_rows, G, kVerifyMaxCols);
+  if (need_device_pointers && B > 0 && (!a->group_start || !a->shared_len))
+    return set_error(PA_ERR_NULL_POINTER, "group_start and shared_len are required");
+  // row parts: at most one worker per SIMD when the library chooses (their pieces all
+  // become partials, so fewer, longer pieces pay off)
+  pa_decode_args rows = b;
+  if (rows.num_workers == 0) {
+    pa_plan p0;
+    plan_decode(&rows, &p0);
+    rows.num_workers = std::min(p0.num_workers, kVerifyMaxWorkers);
+  }
+  pa_plan dplan;
+  plan_decode(&rows, &dplan);
+  const size_t pre_offset = round_up(dplan.workspace_bytes, 256);
+  size_t pbytes = 0;
+  int pw = 0;
+  const size_t punits = B > 0 ? (size_t)a->num_groups * b.num_kv_heads : 0;
+  const int slot_cols = a->max_group_rows * G;
+  if (B > 0) {
+    pw = b.num_workers;
+    if (pw == 0) {
+      const int64_t tiles_upper = (int64_t)punits * ((b.max_seq_len + kVerifyTile - 1) / kVerifyTile);
+      pw = (int)std::min<int64_t>(kVerifyMaxWorkers,
+                                  std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) / kMinTilesPerWorker));
+    }
+    const size_t slots = (punits + pw) * (size_t)slot_cols;
+    pbytes = round_up(2 * punits * sizeof(int32_t), 256) + 2 * round_up(slots * sizeof(float), 256) +
+             round_up(slots * kHeadDim * sizeof(float), 256);
+  }
+  *total_bytes = B > 0 ? pre_offset + pbytes : 0;
+  if (!need_device_pointers || B == 0) return PA_OK;
+  if (!b.workspace || b.workspace_bytes < *total_bytes)
+    return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, the call needs %zu",
+                     b.workspace ? b.workspace_bytes : (size_t)0, *total_bytes);
+  s = make_decode_launch(&rows, dplan, dec);
+  if (s != PA_OK) return s;
+  dec->kv_start = a->shared_len;
+  dec->workers_auto = b.num_workers == 0;
+  dec->min_tiles = kCascadeRowMinTiles;
+  // prefix kernel: items are the groups
+  std::memset(pre, 0, sizeof *pre);
+  pre->q = b.q;
+  pre->k_pool = b.k_pool;
+  pre->v_pool = b.v_pool;
+  pre->block_table = b.block_table;
+  pre->seq_lens = b.seq_lens;
+  pre->group_start = a->group_start;
+  pre->shared_len = a->shared_len;
+  pre->prefix_mode = 1;
+  pre->num_rows = a->num_groups;
+  pre->num_q_heads = b.num_q_heads;
+  pre->num_kv_heads = b.num_kv_heads;
+  pre->block_size = b.block_size;
+  pre->max_blocks_per_seq = b.max_blocks_per_seq;
+  pre->num_workers = pw;
+  pre->workers_auto = b.num_workers == 0;
+  pre->min_tiles = kCascadePrefixMinTiles;
+  pre->slot_cols = slot_cols;
+  pre->out_dtype = b.out_dtype;
+  pre->scale = b.scale;
+  const size_t slots = (punits + pw) * (size_t)slot_cols;
+  char *base = static_cast<char *>(b.workspace) + pre_offset;
+  pre->seg_first = reinterpret_cast<int32_t *>(base);
+  pre->seg_count = pre->seg_first + punits;
+  base += round_up(2 * punits * sizeof(int32_t), 256);
+  pre->part_m = reinterpret_cast<float *>(base);
+  base += round_up(slots * sizeof(float), 256);
+  pre->part_l = reinterpret_cast<float *>(base);
+  base += round_up(slots * sizeof(float), 256);
+  pre->part_acc = reinterpret_cast<float *>(base);
+  // final merge
+  std::memset(mrg, 0, sizeof *mrg);
+  mrg->group_start = a->group_start;
+  mrg->shared_len = a->shared_len;
+  mrg->seg_first = dec->seg_first;
+  mrg->seg_count = dec->seg_count;
+  mrg->part_m = dec->part_m;
+  mrg->part_l = dec->part_l;
+  mrg->part_acc = dec->part_acc;
+  mrg->pseg_first = pre->seg_first;
+  mrg->pseg_count = pre->seg_count;
+  mrg->ppart_m = pre->part_m;
+  mrg->ppart_l = pre->part_l;
+  mrg->ppart_acc = pre->part_acc;
+  mrg->out = b.out;
+  mrg->num_seqs = B;
+  mrg->num_groups = a->num_groups;
+  mrg->num_q_heads = b.num_q_heads;
+  mrg->num_kv_heads = b.num_kv_heads;
+  mrg->slot_cols = slot_cols;
+  mrg->out_dtype = b.out_dtype;
   return PA_OK;
 }
 
@@ -410,6 +522,60 @@ pa_status pa_check_mixed_metadata(const pa_mixed_args *a) {
   }
   return check_rows(&a->base, a->q_start_loc, a->num_decode_rows, a->num_verify_rows, a->max_verify_q_len,
                     a->max_q_len);
+}
+
+pa_status pa_cascade_workspace_size(const pa_cascade_args *a, size_t *bytes) {
+  if (!a || !bytes) return set_error(PA_ERR_NULL_POINTER, "argument is NULL");
+  DecodeLaunch d;
+  VerifyLaunch v;
+  CascadeMergeLaunch m;
+  return plan_cascade(a, false, &d, &v, &m, bytes);
+}
+
+pa_status pa_check_cascade_metadata(const pa_cascade_args *a) {
+  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  DecodeLaunch d;
+  VerifyLaunch v;
+  CascadeMergeLaunch m;
+  size_t total = 0;
+  pa_status s = plan_cascade(a, false, &d, &v, &m, &total);
+  if (s != PA_OK) return s;
+  const pa_decode_args &b = a->base;
+  const int B = b.num_seqs;
+  if (B == 0) return PA_OK;
+  if (!b.seq_lens || !b.block_table || !a->group_start || !a->shared_len)
+    return set_error(PA_ERR_NULL_POINTER, "seq_lens, block_table, group_start and shared_len host copies are required");
+  s = check_rows(&b, nullptr, 0, 0, 0, 0);
+  if (s != PA_OK) return s;
+  const int32_t *gs = a->group_start;
+  if (gs[0] != 0 || gs[a->num_groups] != B)
+    return set_error(PA_ERR_BAD_METADATA, "group_start must run from 0 to num_seqs=%d (got %d .. %d)", B, gs[0],
+                     gs[a->num_groups]);
+  const int bs = b.block_size;
+  for (int k = 0; k < a->num_groups; ++k) {
+    const int r0 = gs[k], r1 = gs[k + 1];
+    if (r1 <= r0) return set_error(PA_ERR_BAD_METADATA, "group %d is empty (group_start not increasing)", k);
+    if (r1 - r0 > a->max_group_rows)
+      return set_error(PA_ERR_BAD_METADATA, "group %d has %d rows > max_group_rows=%d", k, r1 - r0,
+                       a->max_group_rows);
+    const int P = a->shared_len[r0];
+    const int32_t *t0 = b.block_table + (size_t)r0 * b.max_blocks_per_seq;
+    for (int r = r0; r < r1; ++r) {
+      if (a->shared_len[r] != P)
+        return set_error(PA_ERR_BAD_METADATA, "row %d: shared_len=%d differs from its group's %d", r,
+                         a->shared_len[r], P);
+      if (P < 0 || P % bs != 0 || P >= b.seq_lens[r])
+        return set_error(PA_ERR_BAD_METADATA,
+                         "row %d: shared_len=%d must be a multiple of block_size=%d below seq_len=%d", r, P, bs,
+                         b.seq_lens[r]);
+      const int32_t *tr = b.block_table + (size_t)r * b.max_blocks_per_seq;
+      for (int j = 0; j < P / bs; ++j)
+        if (tr[j] != t0[j])
+          return set_error(PA_ERR_BAD_METADATA, "row %d: block %d of the shared prefix is %d, its group's is %d", r,
+                           j, tr[j], t0[j]);
+    }
+  }
+  return PA_OK;
 }
 
 }  // extern "C"

@@ -17,6 +17,10 @@ constexpr int kTargetCUs = 256;          // MI355X compute units (grid planning 
 constexpr int kWorkersPerCU = 8;         // resident decode waves per CU (2 per SIMD)
 constexpr int kMaxWorkers = kTargetCUs * kWorkersPerCU;
 constexpr int kMinTilesPerWorker = 4;    // below this, fewer workers are launched
+constexpr int kCascadeRowMinTiles = 12;  // shared-prefix calls, row parts: every piece is a
+                                         // partial, so pieces are kept longer
+constexpr int kCascadePrefixMinTiles = 2;   // shared-prefix calls, prefix part: few, long units;
+                                            // more workers hide their start-up latency
 constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
 constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
 constexpr int kVerifyMaxWorkers = kTargetCUs * 4;   // one verify wave per SIMD
@@ -36,6 +40,8 @@ struct DecodeLaunch {
   float *part_m;       // [(B*Hkv + workers) * G]   partial slot (unit + worker), head in group
   float *part_l;       // same
   float *part_acc;     // [(B*Hkv + workers) * G][D]
+  const int32_t *kv_start;   // [B] first token each row covers (multiple of bs), or null for 0;
+                             // when set, every piece (whole units too) is left as a partial
   int num_seqs;
   int num_q_heads;
   int num_kv_heads;
@@ -43,6 +49,8 @@ struct DecodeLaunch {
   int max_blocks_per_seq;
   int num_workers;
   int workers_auto;    // 1 when the library chose num_workers (the kernel may use fewer)
+  int min_tiles;       // with workers_auto: at least this many tiles per worker (the plan
+                       // only knows an upper bound of the row lengths)
   int kv_dtype;
   int out_dtype;
   float scale;
@@ -80,16 +88,49 @@ struct VerifyLaunch {
   float *part_m;                 // [(rows*Hkv + workers) * slot_cols] partial slot (unit + worker), column
   float *part_l;
   float *part_acc;               // [... * slot_cols][D]
-  int first_row;                 // first verify row
-  int num_rows;                  // verify rows
+  const int32_t *group_start;    // prefix mode: [num_rows + 1] rows of each group
+  const int32_t *shared_len;     // prefix mode: [B] shared prefix tokens of each row
+  int prefix_mode;               // 0: items are verify rows (causal, own cache);
+                                 // 1: items are groups of decode rows over their shared prefix
+                                 //    (no mask inside the prefix; every piece left as a partial)
+  int first_row;                 // first verify row (verify mode)
+  int num_rows;                  // items: verify rows, or groups
   int num_q_heads;
   int num_kv_heads;
   int block_size;
   int max_blocks_per_seq;
   int num_workers;
+  int workers_auto;              // 1 when the library chose num_workers (the kernel may use fewer)
+  int min_tiles;                 // with workers_auto: at least this many tiles per worker
   int slot_cols;                 // max_verify_q_len * G (<= kVerifyMaxCols)
   int out_dtype;
   float scale;
+};
+
+// Final merge of a shared-prefix decode call: for every (row, query head), the
+// pieces of the row's own part (decode-kernel partials, slot (unit + worker) * G + head)
+// and of its group's shared prefix (prefix-kernel partials, slot (unit + worker) *
+// slot_cols + column).
+struct CascadeMergeLaunch {
+  const int32_t *group_start;
+  const int32_t *shared_len;
+  const int32_t *seg_first;      // row parts: [B*Hkv]
+  const int32_t *seg_count;
+  const float *part_m;
+  const float *part_l;
+  const float *part_acc;
+  const int32_t *pseg_first;     // prefixes: [groups*Hkv]
+  const int32_t *pseg_count;
+  const float *ppart_m;
+  const float *ppart_l;
+  const float *ppart_acc;
+  void *out;
+  int num_seqs;
+  int num_groups;
+  int num_q_heads;
+  int num_kv_heads;
+  int slot_cols;
+  int out_dtype;
 };
 
 struct AppendLaunch {
@@ -121,6 +162,11 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decod
                      size_t *total_bytes);
 pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_offset,
                              VerifyLaunch *V);
+// Checks a shared-prefix decode call and resolves its three launches (prefix kernel,
+// row-part decode kernel, final merge) over the caller's workspace; with
+// need_device_pointers false only the sizes are computed.
+pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, DecodeLaunch *dec,
+                       VerifyLaunch *pre, CascadeMergeLaunch *mrg, size_t *total_bytes);
 int tile_tokens(int kv_dtype);
 
 // Kernel launchers (decode.hip, prefill.hip, verify.hip, append.hip).  Return 0 on success, else the
@@ -131,6 +177,7 @@ int launch_prefill(const PrefillLaunch &L, void *stream);
 int launch_append(const AppendLaunch &L, void *stream);
 int launch_verify_partials(const VerifyLaunch &V, void *stream);
 int launch_verify_merge(const VerifyLaunch &V, void *stream);
+int launch_cascade_merge(const CascadeMergeLaunch &M, void *stream);
 const char *hip_error_name(int code);
 
 }  // namespace pa

@@ -118,7 +118,10 @@ __device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
 }
 
 // NCB: 16-column blocks of query columns (1: up to 16 columns, 2: up to 32).
-template <int NCB, bool OUT_BF16>
+// PREFIX: the items are groups of decode rows and their shared prefix (the query
+// columns are the group rows' queries, nothing is masked inside the prefix, and every
+// piece is left as a partial for the final merge); else the items are verify rows.
+template <int NCB, bool OUT_BF16, bool PREFIX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void verify_kernel(VerifyLaunch p) {
   __shared__ __attribute__((aligned(16))) char s_vt[NW][VT_BYTES];
@@ -139,16 +142,30 @@ void verify_kernel(VerifyLaunch p) {
   const int dg = lane >> 2;                // ... and 8-element group
   char *vt = s_vt[wave];
 
-  // ---- this worker's share of the flattened (row, kv head, tile) space ----
-  const int *lens = p.seq_lens + p.first_row;
+  // tokens each item covers (a group's shared prefix may be empty: no tiles)
+  auto len_of = [&](int r) -> int {
+    if constexpr (PREFIX) return p.shared_len[p.group_start[r]];
+    else return p.seq_lens[p.first_row + r];
+  };
+
+  // ---- this worker's share of the flattened (item, kv head, tile) space ----
   long long W = 0;
+  int n_first = 0, incl_first = 0;         // the first 64 rows' counts, kept for the search below
   for (int base = 0; base < R; base += 64) {
     const int r = base + lane;
-    const int n = r < R ? (lens[r] + TILE - 1) / TILE : 0;
-    W += __builtin_amdgcn_readlane(wave_inclusive_scan(n, lane), 63);
+    const int n = r < R ? (len_of(r) + TILE - 1) / TILE : 0;
+    const int incl = wave_inclusive_scan(n, lane);
+    if (base == 0) {
+      n_first = n;
+      incl_first = incl;
+    }
+    W += __builtin_amdgcn_readlane(incl, 63);
   }
   W *= Hkv;
-  const int nw = (int)min((long long)nworkers, W);
+  // the plan sized the launch for items of max_seq_len; shorter items get fewer workers
+  int nwk = nworkers;
+  if (p.workers_auto) nwk = (int)min((long long)nwk, max(1LL, W / p.min_tiles));
+  const int nw = (int)min((long long)nwk, W);
   if (worker >= nw) return;
   const long long x0 = (long long)worker * W / nw;
   const long long x1 = (long long)(worker + 1) * W / nw;
@@ -160,8 +177,8 @@ void verify_kernel(VerifyLaunch p) {
     long long before = 0;
     for (int base = 0; base < R; base += 64) {
       const int r = base + lane;
-      const int n = r < R ? (lens[r] + TILE - 1) / TILE : 0;
-      const int incl = wave_inclusive_scan(n, lane);
+      const int n = base == 0 ? n_first : (r < R ? (len_of(r) + TILE - 1) / TILE : 0);
+      const int incl = base == 0 ? incl_first : wave_inclusive_scan(n, lane);
       const long long lo = before + (long long)(incl - n) * Hkv;
       const long long hi = before + (long long)incl * Hkv;
       const unsigned long long hit = __builtin_amdgcn_ballot_w64(x0 >= lo && x0 < hi && n > 0);
@@ -181,7 +198,7 @@ void verify_kernel(VerifyLaunch p) {
   const size_t phys_stride = (size_t)Hkv * page_bytes;
   const float qk_scale = p.scale * kLog2e;
 
-  int L = lens[rb];
+  int L = len_of(rb);
   int nb = (L + TILE - 1) / TILE;
   int g = (int)((x0 - rowstart) / nb);
   int t0 = (int)((x0 - rowstart) % nb);
@@ -191,14 +208,16 @@ void verify_kernel(VerifyLaunch p) {
   while (x < x1) {
     const int cnt = (int)min((long long)(nb - t0), x1 - x);
     const int u = rb * Hkv + g;
-    const int row = p.first_row + rb;
+    // the item's first row: its block-table row, and its first query row
+    const int row = PREFIX ? p.group_start[rb] : p.first_row + rb;
     if (t0 == 0 && lane == 0) {
       p.seg_first[u] = worker;
       p.seg_count[u] = worker_of(ustart + nb - 1) - worker + 1;
     }
-    const bool whole = t0 == 0 && cnt == nb;
-    const int qbase = p.q_start_loc[row];
-    const int n = p.q_start_loc[row + 1] - qbase;
+    const bool whole = !PREFIX && t0 == 0 && cnt == nb;
+    // decode rows have one query each, at their own row index
+    const int qbase = PREFIX ? row : p.q_start_loc[row];
+    const int n = (PREFIX ? p.group_start[rb + 1] : p.q_start_loc[row + 1]) - qbase;
     const int ncols = n << log2G;
     const int tok_begin = t0 * TILE;
     const int tok_end = min((t0 + cnt) * TILE, L);
@@ -216,14 +235,14 @@ void verify_kernel(VerifyLaunch p) {
     for (int cb = 0; cb < NCB; ++cb) {
       const int c = 16 * cb + lq;
       const int qi = c >> log2G;
-      lim[cb] = c < ncols ? L - n + qi : L - 1;
+      lim[cb] = (c < ncols && !PREFIX) ? L - n + qi : L - 1;
       const __bf16 *qp = static_cast<const __bf16 *>(p.q) +
                          ((size_t)(qbase + qi) * Hq + g * G + (c & (G - 1))) * D + 8 * lg;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
         qb[cb][kk] = c < ncols ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
     }
-    const int mask_from = L - n;           // tiles reaching past this position need the mask
+    const int mask_from = PREFIX ? L - 1 : L - n;   // tiles reaching past this need the mask
     const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
     const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
 
@@ -414,8 +433,12 @@ void verify_kernel(VerifyLaunch p) {
       g = 0;
       ++rb;
       if (x < x1) {
-        L = lens[rb];
+        L = len_of(rb);
         nb = (L + TILE - 1) / TILE;
+        while (nb == 0) {                  // items without tiles (empty shared prefix)
+          L = len_of(++rb);
+          nb = (L + TILE - 1) / TILE;
+        }
       }
     }
   }
@@ -459,13 +482,13 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   }
 }
 
-template <int NCB>
+template <int NCB, bool PREFIX>
 int launch_ncb(const VerifyLaunch &V, hipStream_t st) {
   dim3 grid((V.num_workers + NW - 1) / NW);
   if (V.out_dtype == PA_BF16)
-    hipLaunchKernelGGL((verify_kernel<NCB, true>), grid, dim3(NT), 0, st, V);
+    hipLaunchKernelGGL((verify_kernel<NCB, true, PREFIX>), grid, dim3(NT), 0, st, V);
   else
-    hipLaunchKernelGGL((verify_kernel<NCB, false>), grid, dim3(NT), 0, st, V);
+    hipLaunchKernelGGL((verify_kernel<NCB, false, PREFIX>), grid, dim3(NT), 0, st, V);
   return (int)hipGetLastError();
 }
 
@@ -473,7 +496,8 @@ int launch_ncb(const VerifyLaunch &V, hipStream_t st) {
 
 int launch_verify_partials(const VerifyLaunch &V, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return V.slot_cols <= 16 ? launch_ncb<1>(V, st) : launch_ncb<2>(V, st);
+  if (V.prefix_mode) return V.slot_cols <= 16 ? launch_ncb<1, true>(V, st) : launch_ncb<2, true>(V, st);
+  return V.slot_cols <= 16 ? launch_ncb<1, false>(V, st) : launch_ncb<2, false>(V, st);
 }
 
 int launch_verify_merge(const VerifyLaunch &V, void *stream) {

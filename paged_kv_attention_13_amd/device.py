@@ -28,4 +28,7 @@ def to_device(w, device="cuda"):
         "k_scale": dev(w.k_scale) if w.k_scale is not None else None,
         "v_scale": dev(w.v_scale) if w.v_scale is not None else None,
     }
+    if getattr(w, "group_start", None) is not None:
+        out["group_start"] = dev(w.group_start)
+        out["shared_len"] = dev(w.shared_len)
     return out

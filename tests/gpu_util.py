@@ -49,3 +49,19 @@ def compare(got, ref, tol, rel_tol=TOL_REL_L2, what=""):
     assert mx <= tol, f"{what}: max abs err {mx:.3e} > {tol}"
     assert rel <= rel_tol, f"{what}: relative L2 err {rel:.3e} > {rel_tol}"
     return mx, rel
+
+
+def run_cascade(w, out_dtype=None, num_workers=0, dev=None, max_group_rows=None):
+    """pa_decode_cascade on a shared-prefix workload (``w.group_start``, ``w.shared_len``)."""
+    import torch
+    from paged_kv_attention_13_amd import binding
+    from paged_kv_attention_13_amd.device import to_device
+    d = dev or to_device(w)
+    odt = {None: None, "f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    if max_group_rows is None:
+        max_group_rows = int(np.diff(w.group_start).max())
+    out = binding.decode_cascade(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                 d["group_start"], d["shared_len"], w.scale, max_seq_len=w.max_seq_len,
+                                 max_group_rows=max_group_rows, out_dtype=odt, num_workers=num_workers)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)

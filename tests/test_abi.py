@@ -55,6 +55,11 @@ def test_struct_layout_matches_header(b):
     assert b.MixedArgs.num_verify_rows.offset == nb + 8 + 3 * 4
     assert b.MixedArgs.max_verify_q_len.offset == nb + 8 + 4 * 4
     assert ctypes.sizeof(b.MixedArgs) == nb + 8 + 5 * 4 + 4      # padded to 8 bytes
+    assert b.CascadeArgs.group_start.offset == nb
+    assert b.CascadeArgs.shared_len.offset == nb + 8
+    assert b.CascadeArgs.num_groups.offset == nb + 16
+    assert b.CascadeArgs.max_group_rows.offset == nb + 20
+    assert ctypes.sizeof(b.CascadeArgs) == nb + 24
 
 
 def _args(b, **kw):
@@ -227,6 +232,103 @@ def test_mixed_workspace_holds_verify_partials(b):
     assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n3)) == 0
     slots = (units + 3) * 16
     assert n2.value == r256(n3.value) + r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 512)
+
+
+def _cascade_args(b, **kw):
+    c = b.CascadeArgs()
+    c.base = _args(b, num_seqs=4, max_seq_len=128)
+    c.group_start = c.shared_len = 0x10000
+    c.num_groups = 2
+    c.max_group_rows = 3
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_groups=0), "PA_ERR_BAD_SHAPE"),
+    (dict(num_groups=5), "PA_ERR_BAD_SHAPE"),                 # more groups than rows
+    (dict(max_group_rows=0), "PA_ERR_UNSUPPORTED"),
+    (dict(max_group_rows=9), "PA_ERR_UNSUPPORTED"),           # 9 rows x group 4 > 32 columns
+    (dict(group_start=None), "PA_ERR_NULL_POINTER"),
+    (dict(shared_len=None), "PA_ERR_NULL_POINTER"),
+    (dict(), "PA_ERR_WORKSPACE_TOO_SMALL"),                   # no workspace
+])
+def test_cascade_validation(b, kw, status):
+    c = _cascade_args(b, **kw)
+    assert b.STATUS_NAMES[b.LIB.pa_decode_cascade(ctypes.byref(c), None)] == status
+
+
+def test_cascade_needs_bf16(b):
+    c = _cascade_args(b)
+    c.base.kv_dtype = b.PA_FP8_E4M3
+    c.base.k_scale = c.base.v_scale = 0x10000
+    assert b.STATUS_NAMES[b.LIB.pa_decode_cascade(ctypes.byref(c), None)] == "PA_ERR_UNSUPPORTED"
+
+
+def test_cascade_workspace_size(b):
+    """Decode part (every row's own tokens) then the prefix part, 256-byte aligned."""
+    c = _cascade_args(b)
+    n = ctypes.c_size_t()
+    assert b.LIB.pa_cascade_workspace_size(ctypes.byref(c), ctypes.byref(n)) == 0
+    r256 = lambda x: (x + 255) // 256 * 256
+    c.base.num_workers = min(b.plan(c.base).num_workers, 1024)   # row parts: one worker per SIMD at most
+    dec = b.plan(c.base).workspace_bytes
+    c.base.num_workers = 0
+    units = 2 * 8
+    workers = min(1024, max(1, (units * 4 + 3) // 4))
+    slots = (units + workers) * 3 * 4
+    assert n.value == r256(dec) + r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 512)
+
+
+def _cmeta(b, table, lens, gs, shared, max_group_rows=4, **kw):
+    args = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, num_blocks=20, max_seq_len=64)
+    args.update(kw)
+    b.check_cascade_metadata(np.array(table), np.array(lens), np.array(gs), np.array(shared),
+                             max_group_rows=max_group_rows, **args)
+
+
+def test_cascade_metadata_checker(b):
+    table = [[0, 1, 2, -1], [0, 1, 3, -1], [4, 5, -1, -1]]
+    _cmeta(b, table, [40, 33, 20], [0, 2, 3], [32, 32, 0])
+    _cmeta(b, table, [40, 33, 20], [0, 2, 3], [16, 16, 16])            # a shorter shared part is fine
+    with pytest.raises(b.PagedAttentionError, match="differs"):
+        _cmeta(b, table, [40, 33, 20], [0, 2, 3], [32, 16, 0])
+    with pytest.raises(b.PagedAttentionError, match="multiple of block_size"):
+        _cmeta(b, table, [40, 33, 20], [0, 2, 3], [24, 24, 0])
+    with pytest.raises(b.PagedAttentionError, match="below seq_len"):
+        _cmeta(b, table, [40, 32, 20], [0, 2, 3], [32, 32, 0])         # row 1 would have no own token
+    with pytest.raises(b.PagedAttentionError, match="shared prefix"):
+        _cmeta(b, [[0, 1, 2, 6], [0, 1, 3, 7], [4, 5, -1, -1]], [60, 60, 20], [0, 2, 3],
+               [48, 48, 0])                                            # third block differs
+    with pytest.raises(b.PagedAttentionError, match="empty"):
+        _cmeta(b, table, [40, 33, 20], [0, 2, 2, 3], [32, 32, 0])
+    with pytest.raises(b.PagedAttentionError, match="max_group_rows"):
+        _cmeta(b, table, [40, 33, 20], [0, 2, 3], [32, 32, 0], max_group_rows=1)
+    with pytest.raises(b.PagedAttentionError, match="group_start"):
+        _cmeta(b, table, [40, 33, 20], [0, 2, 2], [32, 32, 0])
+
+
+def test_shared_prefix_inputs_pass_the_checker(b):
+    import pa_inputs
+    w = pa_inputs.make_shared_prefix_workload(name="t", group_sizes=[3, 1, 2, 8], shared_lens=[32, 0, 48, 64],
+                                              own_lens=[1, 5, 17, 3, 16, 40] + [7] * 8, prefix_ids=[0, 1, 0, 2],
+                                              seed=1, extra_blocks=2)
+    b.check_cascade_metadata(w.block_table, w.seq_lens, w.group_start, w.shared_len, max_group_rows=8,
+                             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                             num_blocks=w.num_blocks, max_seq_len=w.max_seq_len)
+    # own blocks belong to one row only; prefix blocks only to rows of groups with that prefix
+    owners = {}
+    for r in range(w.num_seqs):
+        nb = (int(w.seq_lens[r]) + 15) // 16
+        for j in range(nb):
+            owners.setdefault(int(w.block_table[r, j]), set()).add(r)
+    for r in range(w.num_seqs):
+        nsh = int(w.shared_len[r]) // 16
+        nb = (int(w.seq_lens[r]) + 15) // 16
+        for j in range(nsh, nb):
+            assert owners[int(w.block_table[r, j])] == {r}
+    assert set(w.block_table[0, :2]) == set(w.block_table[4, :2])     # prefix id 0 shared across groups
 
 
 def _meta(b, table, lens, **kw):

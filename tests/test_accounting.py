@@ -75,7 +75,7 @@ def test_generator_is_deterministic_and_shaped():
     assert len(set(used.tolist())) == len(used)                          # no two rows share a block
 
 
-@pytest.mark.parametrize("i", [1, 2, 4, 5, 6])
+@pytest.mark.parametrize("i", [1, 2, 4, 5, 6, 7])
 def test_named_workload_lengths(i):
     L, ql = pa_inputs.workload_lengths(i)
     if i == 1:
@@ -92,6 +92,8 @@ def test_named_workload_lengths(i):
         assert np.all(L[96:] >= 256) and np.all(L[96:] <= 2048 + 256)
     if i == 6:
         assert len(L) == 55 and np.all(L == 8192) and np.all(ql == 4)
+    if i == 7:
+        assert len(L) == 64 and L.min() >= 1488 + 313 and L.max() <= 1488 + 312 + 250
 
 
 def test_fp8_quantiser_roundtrip_bound():

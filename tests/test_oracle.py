@@ -18,6 +18,7 @@ import torch
 import oracle
 from oracle import attention as pa_mod
 from pa_inputs import make_workload, random_block_table
+import pa_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -406,3 +407,60 @@ def test_planted_attend_mistakes_are_caught(monkeypatch, mistake):
     assert not _sdpa_pin_passes()
     monkeypatch.setattr(pa_mod, "attend_rows", orig)
     assert _sdpa_pin_passes()
+
+
+# ----------------------------------------------------------------------------
+# shared prefixes: rows whose tables alias the same physical prefix blocks
+# ----------------------------------------------------------------------------
+
+def test_aliased_prefix_equals_private_copies():
+    """Rows pointing at shared prefix blocks get exactly what they get from private copies.
+
+    Prefix reuse ("How does TensorRT-LLM work", section "The paged KV cache")
+    stores an identical beginning once; attention must not notice.  The copy
+    gives every row its own blocks with the same contents, relabelled in the
+    table.
+    """
+    w = pa_inputs.make_shared_prefix_workload(name="alias", group_sizes=[3, 2, 1], shared_lens=[32, 48, 16],
+                                              own_lens=[1, 20, 5, 33, 2, 9], prefix_ids=[0, 0, 1],
+                                              num_q_heads=4, num_kv_heads=2, head_dim=8, seed=4)
+    ref = oracle.paged_attention_workload(w)
+    bs = w.block_size
+    used = [(r, j) for r in range(w.num_seqs) for j in range((int(w.seq_lens[r]) + bs - 1) // bs)]
+    kp = np.concatenate([w.k_pool[w.block_table[r, j]][None] for r, j in used])
+    vp = np.concatenate([w.v_pool[w.block_table[r, j]][None] for r, j in used])
+    table = np.full_like(w.block_table, -1)
+    for i, (r, j) in enumerate(used):
+        table[r, j] = i
+    assert len(set(table[table >= 0].tolist())) == len(used)           # now nothing is shared
+    got = oracle.paged_attention(w.q, w.q_fmt, kp, vp, w.kv_fmt, table, w.seq_lens, bs, w.num_q_heads,
+                                 w.num_kv_heads, w.scale, w.q_lens)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_split_at_shared_boundary_merges_exactly():
+    """Attention over [prefix | own part] equals the log-sum-exp merge of the two parts.
+
+    This is the identity a shared-prefix call relies on (the split-context merge
+    named Flash-Decoding, "Introduction to TensorRT-LLM", section "Core
+    Optimization Technologies"): with s_j = scale q.k_j over part j,
+    m_j = max s_j, l_j = sum exp(s_j - m_j), a_j = sum exp(s_j - m_j) v_j,
+    o = sum_j exp(m_j - M) a_j / sum_j exp(m_j - M) l_j.  Checked in fp64 against
+    the oracle for every split point.
+    """
+    rng = np.random.default_rng(3)
+    L, D = 40, 8
+    q = rng.standard_normal(D)
+    K = rng.standard_normal((L, D))
+    V = rng.standard_normal((L, D))
+    full = oracle.attend_rows(q[None], K, V, 0.3, L - 1)[0]
+    for P in range(1, L):
+        parts = []
+        for lo, hi in ((0, P), (P, L)):
+            s = 0.3 * K[lo:hi] @ q
+            m = s.max()
+            e = np.exp(s - m)
+            parts.append((m, e.sum(), e @ V[lo:hi]))
+        M = max(p[0] for p in parts)
+        o = sum(np.exp(m - M) * a for m, _, a in parts) / sum(np.exp(m - M) * l for m, l, _ in parts)
+        np.testing.assert_allclose(o, full, rtol=1e-13, atol=1e-14)
