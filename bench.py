@@ -42,11 +42,15 @@ def parse():
                     help="decode work split into this many waves (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "append-fp8", "cascade"],
+    ap.add_argument("--loop-batch", type=int, default=1,
+                    help="--op loop: decode rows in the steady batch")
+    ap.add_argument("--op", default="decode", choices=["decode", "append", "append-fp8", "cascade", "loop"],
                     help="decode: the attention call of --workload (default); append / append-fp8: "
                          "writing the mixed workload's 2,144 new tokens (96 decode + 8 x 256 prefill) "
                          "into their cache slots, bf16 -> bf16 or bf16 -> FP8-E4M3; cascade: the "
-                         "shared-prefix decode call on workload 7, with pa_decode on the same rows beside it")
+                         "shared-prefix decode call on workload 7, with pa_decode on the same rows beside it; "
+                         "loop: 32 layers of append + decode per step driven by the host scheduler, launched "
+                         "eagerly and replayed as one HIP graph")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed loop, run one device-to-device copy of this many MiB "
                          "(a plain copy kernel of known size, to calibrate HBM byte counters)")
@@ -259,6 +263,80 @@ def bench_cascade(args):
     }), flush=True)
 
 
+def bench_loop(args):
+    """Decode steps of a 32-layer attention stack at small batch: eager launches vs one graph replay."""
+    import numpy as np
+    import torch
+
+    from paged_kv_attention_13_amd.loop import DecodeLoop
+
+    B, layers, prompt, bs = args.loop_batch, 32, 511, 16
+    mk = lambda: DecodeLoop(num_layers=layers, num_blocks=B * 64 + 8, block_size=bs,  # noqa: E731
+                            max_blocks_per_seq=64, max_batch_size=B, max_num_tokens=B * prompt,
+                            prefix_reuse=False)
+    loops = {"eager": mk(), "graph": mk()}
+    rng = np.random.default_rng(11)
+    for lp in loops.values():
+        for r in range(B):
+            lp.kvm.add_request(r, rng.integers(0, 32000, size=prompt), args.warmup + args.steps + 5)
+        for layer in range(layers):
+            for t in (lp.q[layer], lp.k_new[layer], lp.v_new[layer]):
+                t.normal_()
+        b = lp.schedule()                        # the whole prompt in one pass
+        lp.run_batch(b)
+        torch.cuda.synchronize()
+        lp.complete(np.zeros(b.num_rows, np.int32))
+        lp.prepare_decode(B)
+    res = {}
+    for mode, lp in loops.items():
+        step_ms, gpu_ms = [], []
+        for i in range(args.warmup + args.steps):
+            b = lp.schedule()
+            assert b.num_rows == B and b.num_decode_rows == B
+            lp.stage(b)
+            if mode == "graph" and lp.graph is None:
+                lp.capture_decode_step()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record()
+            if mode == "graph":
+                lp.decode_step_graph()
+            else:
+                lp.decode_step_eager()
+            e1.record()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            lp.complete(np.zeros(B, np.int32))
+            if i >= args.warmup:
+                step_ms.append((t1 - t0) * 1e3)
+                gpu_ms.append(e0.elapsed_time(e1))
+        res[mode] = {"ms_per_step": float(np.mean(step_ms)), "gpu_ms": float(np.mean(gpu_ms)),
+                     "p90_ms": float(np.percentile(step_ms, 90))}
+    ctx = prompt + args.warmup + args.steps // 2
+    kv = layers * B * ctx * 8 * 128 * 2 * 2
+    g = res["graph"]["ms_per_step"]
+    print(json.dumps({
+        "metric": "decode-loop step latency, 32 layers of paged KV append + attention (graph replay)",
+        "value": round(B / (g * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(g, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic (seeded N(0,1) q/K/V; {B} request(s) with a {prompt}-token prompt, then decode)",
+        "config": {"workload": f"decode loop B{B} ctx~{ctx} 32 layers bs16", "batch": B, "layers": layers,
+                   "q_heads": 32, "kv_heads": 8, "head_dim": 128, "block_size": bs,
+                   "launches_per_step_eager": layers * 3 + 4},
+        "eager": {k: round(v, 5) for k, v in res["eager"].items()},
+        "graph": {k: round(v, 5) for k, v in res["graph"].items()},
+        "graph_speedup": round(res["eager"]["ms_per_step"] / g, 3),
+        "kv_bytes_per_step": int(kv),
+        "roofline": {"bound": "hbm", "achieved": round(kv / (res["graph"]["gpu_ms"] * 1e-3) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kv / (res["graph"]["gpu_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "graph replay (32 x append + decode + merge)",
+                     "kernel_ms_mean": round(res["graph"]["gpu_ms"], 5), "bytes_per_launch": int(kv)},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -269,6 +347,9 @@ def main():
 
     if args.op == "cascade":
         bench_cascade(args)
+        return
+    if args.op == "loop":
+        bench_loop(args)
         return
     if args.op != "decode":
         bench_append(args)
