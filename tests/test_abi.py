@@ -119,7 +119,9 @@ def test_plan_choices(b):
     assert p.num_workers == 2048 and p.tile_tokens == 16
     units = 55 * 8
     slots = (units + 2048) * 4
-    assert p.workspace_bytes >= 2 * units * 4 + slots * (128 + 2) * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+    # (first worker, count) records, then m, l and acc of every partial slot
+    assert p.workspace_bytes == r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 512)
     # FP8 KV uses 32-token tiles
     a.kv_dtype = 2
     a.k_scale = a.v_scale = 0x10000
