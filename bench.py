@@ -224,8 +224,9 @@ def bench_cascade(args):
                                   max_group_rows=rows_per_group, out=out, num_workers=args.num_workers)
     ws = torch.empty(max(binding.cascade_workspace_bytes(c), 16), dtype=torch.uint8, device="cuda")
     c.base.workspace, c.base.workspace_bytes = ws.data_ptr(), ws.numel()
+    out_dec = torch.empty_like(out)
     a = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], w.scale,
-                                 max_seq_len=w.max_seq_len, out=torch.empty_like(out),
+                                 max_seq_len=w.max_seq_len, out=out_dec,
                                  num_workers=args.num_workers)
     wsd = torch.empty(max(binding.plan(a).workspace_bytes, 16), dtype=torch.uint8, device="cuda")
     a.workspace, a.workspace_bytes = wsd.data_ptr(), wsd.numel()

@@ -178,6 +178,21 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _hold(struct, *objs):
+    """Keep the tensors whose addresses a struct carries alive as long as the struct.
+
+    The C structs hold plain addresses; without this a temporary tensor passed in
+    (``out=torch.empty(...)``) would be freed at once and its memory handed to the
+    next allocation while the library still writes there.
+    """
+    keep = getattr(struct, "_keep", None)
+    if keep is None:
+        keep = []
+        struct._keep = keep
+    keep.extend(o for o in objs if o is not None)
+    return struct
+
+
 def make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq_len: int,
                      k_scale=None, v_scale=None, out=None, num_workers: int = 0,
                      workspace=None) -> DecodeArgs:
@@ -206,7 +221,7 @@ def make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq
     if workspace is not None:
         a.workspace = _ptr(workspace)
         a.workspace_bytes = workspace.numel() * workspace.element_size()
-    return a
+    return _hold(a, q, k_pool, v_pool, k_scale, v_scale, block_table, seq_lens, out, workspace)
 
 
 def plan(args: DecodeArgs) -> Plan:
@@ -261,15 +276,16 @@ def make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale
                     num_workers: int = 0, num_verify_rows: int = 0,
                     max_verify_q_len: int = 0) -> MixedArgs:
     m = MixedArgs()
-    m.base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
-                              out=out, num_workers=num_workers)
+    base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
+                            out=out, num_workers=num_workers)
+    m.base = base
     m.q_start_loc = _ptr(q_start_loc)
     m.total_q = int(q.shape[0])
     m.num_decode_rows = int(num_decode_rows)
     m.max_q_len = int(max_q_len)
     m.num_verify_rows = int(num_verify_rows)
     m.max_verify_q_len = int(max_verify_q_len)
-    return m
+    return _hold(m, *base._keep, q_start_loc)
 
 
 def mixed_workspace_bytes(m: MixedArgs) -> int:
@@ -347,13 +363,14 @@ def check_mixed_metadata(block_table, seq_lens, q_start_loc, *, num_decode_rows:
 def make_cascade_args(q, k_pool, v_pool, block_table, seq_lens, group_start, shared_len, scale, *,
                       max_seq_len: int, max_group_rows: int, out=None, num_workers: int = 0) -> CascadeArgs:
     c = CascadeArgs()
-    c.base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
-                              out=out, num_workers=num_workers)
+    base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
+                            out=out, num_workers=num_workers)
+    c.base = base
     c.group_start = _ptr(group_start)
     c.shared_len = _ptr(shared_len)
     c.num_groups = int(group_start.shape[0]) - 1
     c.max_group_rows = int(max_group_rows)
-    return c
+    return _hold(c, *base._keep, group_start, shared_len)
 
 
 def cascade_workspace_bytes(c: CascadeArgs) -> int:
@@ -424,7 +441,7 @@ def make_append_args(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=N
     a.v_pool = _ptr(v_pool)
     a.k_scale = _ptr(k_scale)
     a.v_scale = _ptr(v_scale)
-    return a
+    return _hold(a, k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale)
 
 
 def append(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None, stream=None) -> None:

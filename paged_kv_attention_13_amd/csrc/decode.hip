@@ -1,4 +1,5 @@
-// Decode attention over a paged KV cache on gfx950 (CDNA4), VALU path.
+// Decode attention over a paged KV cache on gfx950 (CDNA4), VALU path (fp32 and bf16
+// pools; FP8 pools run on the matrix-core multi-query kernel).
 //
 // What is computed: for every decode row, kv head g and query head h of g's
 // group, softmax(scale * q.K^T) V over the row's whole KV cache, with the
@@ -12,7 +13,7 @@
 // Optimization Technologies".
 //
 // Work decomposition.  The work is the flattened sequence of (row, kv head,
-// 16-token tile) units (32-token tiles for FP8), cut into equal contiguous
+// 16-token tile) units, cut into equal contiguous
 // ranges, one per worker wave; the launch holds about as many waves as the
 // chip keeps resident, so there is no tail of late workgroups and no empty
 // workgroup for short rows.  Each wave streams its range on its own (no LDS,
@@ -29,10 +30,7 @@
 //
 // Arithmetic.  Q.K uses v_dot2c_f32_bf16 (bf16 pairs, fp32 accumulate); the
 // 8 partial sums of a token are combined with three DPP adds (quad xor 1,
-// quad xor 2, half-row mirror).  FP8-E4M3 codes are widened to bf16 in
-// registers (exactly: every E4M3 value is a bf16 value) with
-// v_cvt_scalef32_pk_bf16_fp8; the per-head K scale is folded into the softmax
-// scale and the V scale applied once at the end.  The softmax runs in the
+// quad xor 2, half-row mirror).  The softmax runs in the
 // log2 domain in fp32 registers, one running (max, sum) per 8-lane token
 // group, with lazy rescaling: the running max moves only when a tile's max
 // exceeds it by more than 2^8, which keeps every exp2 argument <= 8 and makes
@@ -67,7 +65,6 @@ constexpr int kDppRowRor8 = 0x128;    // row_ror:8: lane i <- (i+8) mod 16
 template <int KV> struct KvTraits;
 template <> struct KvTraits<PA_F32> { static constexpr int EB = 4, TPL = 2; };
 template <> struct KvTraits<PA_BF16> { static constexpr int EB = 2, TPL = 2; };
-template <> struct KvTraits<PA_FP8_E4M3> { static constexpr int EB = 1, TPL = 4; };
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -78,12 +75,6 @@ __device__ __forceinline__ float dpp(float v) {
 __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
                                          c, false);
-}
-
-// two E4M3 codes (byte pair HI of the dword) -> bf16 pair, exact
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, HI));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -254,8 +245,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) qf[hh][e] = q[hh * D + elem_d<EB>(c, e)];
     }
-    float qk_scale = p.scale * kLog2e;
-    if constexpr (KV == PA_FP8_E4M3) qk_scale *= p.k_scale[g];
+    const float qk_scale = p.scale * kLog2e;
     const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
     const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
 
@@ -297,22 +287,11 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
 #pragma unroll
         for (int i = 0; i < DW; ++i) kd[i] = k[r][i / 4][i % 4];
         if constexpr (kBf) {
-          uint32_t kp[8];
-          if constexpr (KV == PA_BF16) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) kp[i] = kd[i];
-          } else {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              kp[2 * w] = fp8x2_to_bf16x2<false>(kd[w]);
-              kp[2 * w + 1] = fp8x2_to_bf16x2<true>(kd[w]);
-            }
-          }
 #pragma unroll
           for (int hh = 0; hh < G; ++hh) {
             float a = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a = dot2bf(qb[hh][i], kp[i], a);
+            for (int i = 0; i < 8; ++i) a = dot2bf(qb[hh][i], kd[i], a);
             sc[r][hh] = a;
           }
         } else {
@@ -388,37 +367,16 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
             pp[hh] = pack_bf16(pr[r0][hh], pr[r1][hh]);
             l[hh] = dot2bf(pp[hh], kOnes, l[hh]);
           }
-          if constexpr (KV == PA_BF16) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const uint32_t A = v[r0][i / 4][i % 4];
-              const uint32_t Bv = v[r1][i / 4][i % 4];
-              const uint32_t lo = __builtin_amdgcn_perm(Bv, A, 0x05040100u);
-              const uint32_t hi = __builtin_amdgcn_perm(Bv, A, 0x07060302u);
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t A = v[r0][i / 4][i % 4];
+            const uint32_t Bv = v[r1][i / 4][i % 4];
+            const uint32_t lo = __builtin_amdgcn_perm(Bv, A, 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(Bv, A, 0x07060302u);
 #pragma unroll
-              for (int hh = 0; hh < G; ++hh) {
-                acc[hh][2 * i] = dot2bf(lo, pp[hh], acc[hh][2 * i]);
-                acc[hh][2 * i + 1] = dot2bf(hi, pp[hh], acc[hh][2 * i + 1]);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const uint32_t A = v[r0][0][w];
-              const uint32_t Bv = v[r1][0][w];
-              const uint32_t X = __builtin_amdgcn_perm(Bv, A, 0x05010400u);   // a0 b0 a1 b1
-              const uint32_t Y = __builtin_amdgcn_perm(Bv, A, 0x07030602u);   // a2 b2 a3 b3
-              const uint32_t v0 = fp8x2_to_bf16x2<false>(X);
-              const uint32_t v1 = fp8x2_to_bf16x2<true>(X);
-              const uint32_t v2 = fp8x2_to_bf16x2<false>(Y);
-              const uint32_t v3 = fp8x2_to_bf16x2<true>(Y);
-#pragma unroll
-              for (int hh = 0; hh < G; ++hh) {
-                acc[hh][4 * w + 0] = dot2bf(v0, pp[hh], acc[hh][4 * w + 0]);
-                acc[hh][4 * w + 1] = dot2bf(v1, pp[hh], acc[hh][4 * w + 1]);
-                acc[hh][4 * w + 2] = dot2bf(v2, pp[hh], acc[hh][4 * w + 2]);
-                acc[hh][4 * w + 3] = dot2bf(v3, pp[hh], acc[hh][4 * w + 3]);
-              }
+            for (int hh = 0; hh < G; ++hh) {
+              acc[hh][2 * i] = dot2bf(lo, pp[hh], acc[hh][2 * i]);
+              acc[hh][2 * i + 1] = dot2bf(hi, pp[hh], acc[hh][2 * i + 1]);
             }
           }
         }
@@ -506,8 +464,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
         acc[hh][e] = y;
       }
     }
-    float vscale = 1.f;
-    if constexpr (KV == PA_FP8_E4M3) vscale = p.v_scale[g];
+    constexpr float vscale = 1.f;
     // token group hh writes head hh (all 16 of its elements per lane)
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
@@ -611,7 +568,6 @@ int launch_decode_partials(const DecodeLaunch &L, void *stream) {
   switch (L.kv_dtype) {
     case PA_F32: return launch_kv<PA_F32>(L, st);
     case PA_BF16: return launch_kv<PA_BF16>(L, st);
-    case PA_FP8_E4M3: return launch_kv<PA_FP8_E4M3>(L, st);
   }
   return (int)hipErrorInvalidValue;
 }

@@ -27,6 +27,12 @@ pa_status pa_decode_partials(const pa_decode_args *a, void *stream) {
   DecodeLaunch L;
   pa_status s = prepare_decode(a, &plan, &L);
   if (s != PA_OK || a->num_seqs == 0) return s;
+  if (decode_on_mq(a)) {
+    VerifyLaunch V;
+    s = make_decode_mq_launch(a, plan, &V);
+    if (s != PA_OK) return s;
+    return hip_status(launch_verify_partials(V, stream), "decode");
+  }
   return hip_status(launch_decode_partials(L, stream), "decode");
 }
 
@@ -35,17 +41,19 @@ pa_status pa_merge_partials(const pa_decode_args *a, void *stream) {
   DecodeLaunch L;
   pa_status s = prepare_decode(a, &plan, &L);
   if (s != PA_OK || a->num_seqs == 0) return s;
+  if (decode_on_mq(a)) {
+    VerifyLaunch V;
+    s = make_decode_mq_launch(a, plan, &V);
+    if (s != PA_OK) return s;
+    return hip_status(launch_verify_merge(V, stream), "merge");
+  }
   return hip_status(launch_merge(L, stream), "merge");
 }
 
 pa_status pa_decode(const pa_decode_args *a, void *stream) {
-  pa_plan plan;
-  DecodeLaunch L;
-  pa_status s = prepare_decode(a, &plan, &L);
-  if (s != PA_OK || a->num_seqs == 0) return s;
-  s = hip_status(launch_decode_partials(L, stream), "decode");
-  if (s != PA_OK) return s;
-  return hip_status(launch_merge(L, stream), "merge");
+  pa_status s = pa_decode_partials(a, stream);
+  if (s != PA_OK || !a || a->num_seqs == 0) return s;
+  return pa_merge_partials(a, stream);
 }
 
 pa_status pa_append(const pa_append_args *a, void *stream) {
@@ -118,6 +126,14 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     if (s != PA_OK) return s;
   }
   if (d.num_seqs > 0) {
+    if (decode_on_mq(&d)) {
+      VerifyLaunch DV;
+      s = make_decode_mq_launch(&d, plan, &DV);
+      if (s != PA_OK) return s;
+      s = hip_status(launch_verify_partials(DV, stream), "decode");
+      if (s != PA_OK) return s;
+      return hip_status(launch_verify_merge(DV, stream), "merge");
+    }
     s = hip_status(launch_decode_partials(L, stream), "decode");
     if (s != PA_OK) return s;
     return hip_status(launch_merge(L, stream), "merge");

@@ -106,6 +106,9 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
     const int64_t tiles_upper = units * ((a->max_seq_len + tile - 1) / tile);
     nw = (int)std::min<int64_t>(kMaxWorkers, std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) /
                                                                      kMinTilesPerWorker));
+    // FP8 pools run on the multi-query kernel (one column per query head)
+    if (a->kv_dtype == PA_FP8_E4M3)
+      nw = std::min(nw, mq_max_workers(a->kv_dtype, a->num_q_heads / a->num_kv_heads));
   }
   plan->num_workers = nw;
   plan->tile_tokens = tile;
@@ -187,8 +190,8 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decod
     if (a->max_verify_q_len > b.max_seq_len)
       return set_error(PA_ERR_BAD_SHAPE, "max_verify_q_len=%d > max_seq_len=%d", a->max_verify_q_len,
                        b.max_seq_len);
-    if (b.kv_dtype != PA_BF16)
-      return set_error(PA_ERR_UNSUPPORTED, "verify rows need a bf16 KV cache and bf16 q");
+    if (b.q_dtype != PA_BF16)
+      return set_error(PA_ERR_UNSUPPORTED, "verify rows need bf16 q (and a bf16 or FP8 KV cache)");
   }
   if (n_pre > 0) {
     if (a->max_q_len < 1 || a->max_q_len > b.max_seq_len)
@@ -208,7 +211,7 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decod
     int nw = b.num_workers;
     if (nw == 0) {
       const int64_t tiles_upper = units * ((b.max_seq_len + kVerifyTile - 1) / kVerifyTile);
-      nw = (int)std::min<int64_t>(kVerifyMaxWorkers,
+      nw = (int)std::min<int64_t>(mq_max_workers(b.kv_dtype, a->max_verify_q_len * G),
                                   std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) / kMinTilesPerWorker));
     }
     *verify_workers = nw;
@@ -231,6 +234,10 @@ pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_
   V->seq_lens = b.seq_lens;
   V->q_start_loc = a->q_start_loc;
   V->out = b.out;
+  V->k_scale = b.k_scale;
+  V->v_scale = b.v_scale;
+  V->item_kind = 0;
+  V->kv_dtype = b.kv_dtype;
   V->first_row = a->num_decode_rows;
   V->num_rows = a->num_verify_rows;
   V->num_q_heads = b.num_q_heads;
@@ -241,6 +248,7 @@ pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_
   V->workers_auto = b.num_workers == 0;
   V->min_tiles = kMinTilesPerWorker;
   V->slot_cols = a->max_verify_q_len * G;
+  V->unit_cost = kMqUnitCost;
   V->out_dtype = b.out_dtype;
   V->scale = b.scale;
   const size_t units = (size_t)a->num_verify_rows * b.num_kv_heads;
@@ -320,7 +328,8 @@ pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, Deco
   pre->seq_lens = b.seq_lens;
   pre->group_start = a->group_start;
   pre->shared_len = a->shared_len;
-  pre->prefix_mode = 1;
+  pre->item_kind = 1;
+  pre->kv_dtype = PA_BF16;
   pre->num_rows = a->num_groups;
   pre->num_q_heads = b.num_q_heads;
   pre->num_kv_heads = b.num_kv_heads;
@@ -330,6 +339,7 @@ pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, Deco
   pre->workers_auto = b.num_workers == 0;
   pre->min_tiles = kCascadePrefixMinTiles;
   pre->slot_cols = slot_cols;
+  pre->unit_cost = kMqUnitCost;
   pre->out_dtype = b.out_dtype;
   pre->scale = b.scale;
   const size_t slots = (punits + pw) * (size_t)slot_cols;
@@ -363,6 +373,42 @@ pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, Deco
   mrg->num_kv_heads = b.num_kv_heads;
   mrg->slot_cols = slot_cols;
   mrg->out_dtype = b.out_dtype;
+  return PA_OK;
+}
+
+pa_status make_decode_mq_launch(const pa_decode_args *a, const pa_plan &plan, VerifyLaunch *V) {
+  DecodeLaunch L;
+  pa_status s = make_decode_launch(a, plan, &L);
+  if (s != PA_OK) return s;
+  std::memset(V, 0, sizeof *V);
+  V->q = a->q;
+  V->k_pool = a->k_pool;
+  V->v_pool = a->v_pool;
+  V->block_table = a->block_table;
+  V->seq_lens = a->seq_lens;
+  V->out = a->out;
+  V->seg_first = L.seg_first;
+  V->seg_count = L.seg_count;
+  V->part_m = L.part_m;
+  V->part_l = L.part_l;
+  V->part_acc = L.part_acc;
+  V->k_scale = a->k_scale;
+  V->v_scale = a->v_scale;
+  V->item_kind = 2;
+  V->kv_dtype = a->kv_dtype;
+  V->first_row = 0;
+  V->num_rows = a->num_seqs;
+  V->num_q_heads = a->num_q_heads;
+  V->num_kv_heads = a->num_kv_heads;
+  V->block_size = a->block_size;
+  V->max_blocks_per_seq = a->max_blocks_per_seq;
+  V->num_workers = plan.num_workers;
+  V->workers_auto = a->num_workers == 0;
+  V->min_tiles = kMinTilesPerWorker;
+  V->slot_cols = a->num_q_heads / a->num_kv_heads;
+  V->unit_cost = kMqUnitCost;
+  V->out_dtype = a->out_dtype;
+  V->scale = a->scale;
   return PA_OK;
 }
 

@@ -24,6 +24,7 @@ constexpr int kCascadePrefixMinTiles = 2;   // shared-prefix calls, prefix part:
 constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
 constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
 constexpr int kVerifyMaxWorkers = kTargetCUs * 4;   // one verify wave per SIMD
+constexpr int kMqUnitCost = 4;           // multi-query kernel: start-up cost of a unit, in tiles
 
 // Everything a decode launch needs, resolved on the host.
 struct DecodeLaunch {
@@ -77,7 +78,7 @@ struct PrefillLaunch {
 
 struct VerifyLaunch {
   const void *q;                 // [total_q][Hq][D] bf16
-  const void *k_pool;            // bf16 pools
+  const void *k_pool;            // bf16 or FP8 pools
   const void *v_pool;
   const int32_t *block_table;
   const int32_t *seq_lens;
@@ -90,9 +91,13 @@ struct VerifyLaunch {
   float *part_acc;               // [... * slot_cols][D]
   const int32_t *group_start;    // prefix mode: [num_rows + 1] rows of each group
   const int32_t *shared_len;     // prefix mode: [B] shared prefix tokens of each row
-  int prefix_mode;               // 0: items are verify rows (causal, own cache);
+  const float *k_scale;          // [Hkv] (FP8 pools only)
+  const float *v_scale;
+  int item_kind;                 // 0: items are verify rows (causal, own cache);
                                  // 1: items are groups of decode rows over their shared prefix
-                                 //    (no mask inside the prefix; every piece left as a partial)
+                                 //    (no mask inside the prefix; every piece left as a partial);
+                                 // 2: items are decode rows (one query each, at the row index)
+  int kv_dtype;                  // PA_BF16 or PA_FP8_E4M3
   int first_row;                 // first verify row (verify mode)
   int num_rows;                  // items: verify rows, or groups
   int num_q_heads;
@@ -103,6 +108,7 @@ struct VerifyLaunch {
   int workers_auto;              // 1 when the library chose num_workers (the kernel may use fewer)
   int min_tiles;                 // with workers_auto: at least this many tiles per worker
   int slot_cols;                 // max_verify_q_len * G (<= kVerifyMaxCols)
+  int unit_cost;                 // virtual tiles charged per unit in the work split
   int out_dtype;
   float scale;
 };
@@ -162,6 +168,14 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decod
                      size_t *total_bytes);
 pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_offset,
                              VerifyLaunch *V);
+// Decode rows whose pools are FP8 run on the multi-query kernel (one query column per
+// head); this builds that launch over the decode workspace layout.
+pa_status make_decode_mq_launch(const pa_decode_args *a, const pa_plan &plan, VerifyLaunch *V);
+inline bool decode_on_mq(const pa_decode_args *a) { return a->kv_dtype == PA_FP8_E4M3; }
+// Resident multi-query waves: one per SIMD, two for FP8 pools with <= 16 columns.
+inline int mq_max_workers(int kv_dtype, int slot_cols) {
+  return (kv_dtype == PA_FP8_E4M3 && slot_cols <= 16) ? 2 * kVerifyMaxWorkers : kVerifyMaxWorkers;
+}
 // Checks a shared-prefix decode call and resolves its three launches (prefix kernel,
 // row-part decode kernel, final merge) over the caller's workspace; with
 // need_device_pointers false only the sizes are computed.

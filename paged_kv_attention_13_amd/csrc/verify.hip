@@ -33,6 +33,13 @@
 //                   them with byte permutes and writes 16-byte groups at a
 //                   swizzled position (conflict-free for the writes and for
 //                   the MFMA-operand reads).
+// FP8-E4M3 pools: codes are widened to bf16 in registers with
+// v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value is a bf16 value), the
+// per-head K scale folded into the softmax scale and the V scale applied to
+// the result.  A lane loads 16 code bytes = 16 consecutive head-dim elements of
+// one token, which feed two MFMA k steps, so K is read with 16-byte loads; the
+// head-dim order of the contraction is permuted to match (and Q^T is read in
+// the same order), which leaves the dot products unchanged.
 // Three register sets keep two tiles' loads in flight while one is computed;
 // one wave per SIMD (up to 512 registers).  Tokens at or past the row's end
 // are excluded by select and their V zeroed before the transpose, so NaN in
@@ -71,6 +78,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// two E4M3 codes (byte pair HI of the dword) -> bf16 pair, exact
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, HI));
+}
+
+// Items of a launch.
+constexpr int kItemVerify = 0;   // verify rows: q_start_loc gives the queries, causal
+constexpr int kItemPrefix = 1;   // groups of decode rows over their shared prefix
+constexpr int kItemDecode = 2;   // decode rows: one query each, at the row's own index
 
 __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 #pragma unroll
@@ -117,13 +135,24 @@ __device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
   }
 }
 
-// NCB: 16-column blocks of query columns (1: up to 16 columns, 2: up to 32).
-// PREFIX: the items are groups of decode rows and their shared prefix (the query
+// KV: PA_BF16 or PA_FP8_E4M3 pools.  NCB: 16-column blocks of query columns (1: up to
+// 16 columns, 2: up to 32).  ITEM: kItemVerify, kItemDecode, or kItemPrefix (the query
 // columns are the group rows' queries, nothing is masked inside the prefix, and every
-// piece is left as a partial for the final merge); else the items are verify rows.
-template <int NCB, bool OUT_BF16, bool PREFIX>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// piece is left as a partial for the final merge).
+// Waves per SIMD: one (up to 512 registers) -- except FP8 pools with 16 columns, whose
+// smaller tiles fit 256 registers: two waves per SIMD keep twice the bytes in flight.
+template <int KV, int NCB>
+constexpr int mq_waves_per_simd() { return (KV == PA_FP8_E4M3 && NCB == 1) ? 2 : 1; }
+
+template <int KV, int ITEM, int NCB, bool OUT_BF16>
+__global__ __launch_bounds__(NT)
+__attribute__((amdgpu_waves_per_eu(mq_waves_per_simd<KV, NCB>(), mq_waves_per_simd<KV, NCB>())))
 void verify_kernel(VerifyLaunch p) {
+  constexpr bool FP8 = KV == PA_FP8_E4M3;
+  constexpr bool PREFIX = ITEM == kItemPrefix;
+  constexpr int EB = FP8 ? 1 : 2;          // bytes per element
+  constexpr int KR = FP8 ? 4 : 8;          // 16-byte K registers per tile and lane
+  constexpr int VR = FP8 ? 4 : 8;          // 16-byte V registers per tile and lane
   __shared__ __attribute__((aligned(16))) char s_vt[NW][VT_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -138,8 +167,12 @@ void verify_kernel(VerifyLaunch p) {
   const int log2G = __builtin_ctz(G);
   const int lq = lane & 15;                // MFMA row / column index
   const int lg = lane >> 4;                // MFMA lane group
-  const int tqa = lane & 3;                // V loads: token quad ...
-  const int dg = lane >> 2;                // ... and 8-element group
+  // V loads: bf16 -- token quad tqa (+ 4 per 16-token half) and 8-element group dg;
+  //          fp8  -- token quad tq8 (of 8) and 16-element group dg8
+  const int tqa = lane & 3;
+  const int dg = lane >> 2;
+  const int tq8 = lane & 7;
+  const int dg8 = lane >> 3;
   char *vt = s_vt[wave];
 
   // tokens each item covers (a group's shared prefix may be empty: no tiles)
@@ -148,12 +181,22 @@ void verify_kernel(VerifyLaunch p) {
     else return p.seq_lens[p.first_row + r];
   };
 
-  // ---- this worker's share of the flattened (item, kv head, tile) space ----
+  // Each unit counts unit_cost extra virtual tiles ahead of its real ones: starting a
+  // unit (query and block-table loads, filling the load pipeline) costs about that much
+  // time, so a worker given many short units gets fewer tiles.  Virtual tiles are
+  // never loaded; a worker whose range holds only a unit's virtual tiles skips it.
+  const int C = p.unit_cost;
+  auto vtiles = [&](int len) -> int {
+    const int t = (len + TILE - 1) / TILE;
+    return t > 0 ? t + C : 0;
+  };
+
+  // ---- this worker's share of the flattened (item, kv head, virtual tile) space ----
   long long W = 0;
   int n_first = 0, incl_first = 0;         // the first 64 rows' counts, kept for the search below
   for (int base = 0; base < R; base += 64) {
     const int r = base + lane;
-    const int n = r < R ? (len_of(r) + TILE - 1) / TILE : 0;
+    const int n = r < R ? vtiles(len_of(r)) : 0;
     const int incl = wave_inclusive_scan(n, lane);
     if (base == 0) {
       n_first = n;
@@ -177,7 +220,7 @@ void verify_kernel(VerifyLaunch p) {
     long long before = 0;
     for (int base = 0; base < R; base += 64) {
       const int r = base + lane;
-      const int n = base == 0 ? n_first : (r < R ? (len_of(r) + TILE - 1) / TILE : 0);
+      const int n = base == 0 ? n_first : (r < R ? vtiles(len_of(r)) : 0);
       const int incl = base == 0 ? incl_first : wave_inclusive_scan(n, lane);
       const long long lo = before + (long long)(incl - n) * Hkv;
       const long long hi = before + (long long)incl * Hkv;
@@ -194,30 +237,41 @@ void verify_kernel(VerifyLaunch p) {
 
   const int bs = p.block_size;
   const int log2bs = __builtin_ctz(bs);
-  const size_t page_bytes = (size_t)bs * D * 2;
+  const size_t page_bytes = (size_t)bs * D * EB;
   const size_t phys_stride = (size_t)Hkv * page_bytes;
-  const float qk_scale = p.scale * kLog2e;
 
   int L = len_of(rb);
   int nb = (L + TILE - 1) / TILE;
-  int g = (int)((x0 - rowstart) / nb);
-  int t0 = (int)((x0 - rowstart) % nb);
-  long long ustart = rowstart + (long long)g * nb;
+  int vnb = nb + C;
+  int g = (int)((x0 - rowstart) / vnb);
+  int tv = (int)((x0 - rowstart) % vnb);
+  long long ustart = rowstart + (long long)g * vnb;
   long long x = x0;
 
   while (x < x1) {
-    const int cnt = (int)min((long long)(nb - t0), x1 - x);
+    const int cntv = (int)min((long long)(vnb - tv), x1 - x);
+    // the real tiles [t0, t0 + cnt) of this unit in this worker's range
+    const int t0 = max(tv - C, 0);
+    const int cnt = tv + cntv - C - t0;
+    if (cnt > 0) {
     const int u = rb * Hkv + g;
     // the item's first row: its block-table row, and its first query row
     const int row = PREFIX ? p.group_start[rb] : p.first_row + rb;
+    float qk_scale = p.scale * kLog2e;
+    float vscale = 1.f;
+    if constexpr (FP8) {
+      qk_scale *= p.k_scale[g];
+      vscale = p.v_scale[g];
+    }
     if (t0 == 0 && lane == 0) {
       p.seg_first[u] = worker;
-      p.seg_count[u] = worker_of(ustart + nb - 1) - worker + 1;
+      p.seg_count[u] = worker_of(ustart + C + nb - 1) - worker + 1;
     }
     const bool whole = !PREFIX && t0 == 0 && cnt == nb;
     // decode rows have one query each, at their own row index
-    const int qbase = PREFIX ? row : p.q_start_loc[row];
-    const int n = (PREFIX ? p.group_start[rb + 1] : p.q_start_loc[row + 1]) - qbase;
+    const int qbase = ITEM == kItemVerify ? p.q_start_loc[row] : row;
+    const int n = ITEM == kItemVerify ? p.q_start_loc[row + 1] - qbase
+                : ITEM == kItemPrefix ? p.group_start[rb + 1] - row : 1;
     const int ncols = n << log2G;
     const int tok_begin = t0 * TILE;
     const int tok_end = min((t0 + cnt) * TILE, L);
@@ -237,10 +291,13 @@ void verify_kernel(VerifyLaunch p) {
       const int qi = c >> log2G;
       lim[cb] = (c < ncols && !PREFIX) ? L - n + qi : L - 1;
       const __bf16 *qp = static_cast<const __bf16 *>(p.q) +
-                         ((size_t)(qbase + qi) * Hq + g * G + (c & (G - 1))) * D + 8 * lg;
+                         ((size_t)(qbase + qi) * Hq + g * G + (c & (G - 1))) * D;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        qb[cb][kk] = c < ncols ? *reinterpret_cast<const u32x4 *>(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+      for (int kk = 0; kk < 4; ++kk) {
+        // head-dim elements of k step kk held by lane group lg (the order K is loaded in)
+        const int d0 = FP8 ? 16 * (lg + 4 * (kk >> 1)) + 8 * (kk & 1) : 32 * kk + 8 * lg;
+        qb[cb][kk] = c < ncols ? *reinterpret_cast<const u32x4 *>(qp + d0) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     const int mask_from = PREFIX ? L - 1 : L - n;   // tiles reaching past this need the mask
     const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
@@ -261,48 +318,102 @@ void verify_kernel(VerifyLaunch p) {
       for (int db = 0; db < 8; ++db) o[db][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // K[tb][kk]: token ts + 16 tb + lq, elements 32 kk + 8 lg .. +8 (the MFMA A operand)
-    // V[tb][i]:  token ts + 16 tb + 4 tqa + i, elements 8 dg .. +8
-    auto load_tile = [&](int t, u32x4 (&k)[2][4], u32x4 (&v)[2][4]) {
+    // bf16: k[4 tb + kk]: token ts + 16 tb + lq, elements 32 kk + 8 lg .. +8 (an MFMA A operand)
+    //       v[4 tb + i]:  token ts + 16 tb + 4 tqa + i, elements 8 dg .. +8
+    // fp8:  k[2 tb + h]:  token ts + 16 tb + lq, elements 16 (lg + 4 h) .. +16 (two k steps)
+    //       v[i]:         token ts + 4 tq8 + i, elements 16 dg8 .. +16
+    auto load_tile = [&](int t, u32x4 (&k)[KR], u32x4 (&v)[VR]) {
       const int ts = tok_begin + t * TILE;
+      const char *vbase[2];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const int tok0 = ts + 16 * tb;     // 16 tokens inside one page (bs >= 16)
         const int page = min(tok0 >> log2bs, last_page);
         const int phys = __builtin_amdgcn_readlane(tbl, page - chunk_base);
         const char *kp = kpool + (size_t)phys * phys_stride;
-        const char *vp = vpool + (size_t)phys * phys_stride;
-        const uint32_t koff = (uint32_t)(((tok0 + lq) & (bs - 1)) * (D * 2) + 16 * lg);
-        const uint32_t voff = (uint32_t)(((tok0 + 4 * tqa) & (bs - 1)) * (D * 2) + 16 * dg);
+        vbase[tb] = vpool + (size_t)phys * phys_stride;
+        const uint32_t krow = (uint32_t)(((tok0 + lq) & (bs - 1)) * (D * EB));
+        if constexpr (FP8) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          k[tb][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + koff + 64 * kk));
+          for (int h = 0; h < 2; ++h)
+            k[2 * tb + h] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(kp + krow + 16 * (lg + 4 * h)));
+        } else {
+          const uint32_t voff = (uint32_t)(((tok0 + 4 * tqa) & (bs - 1)) * (D * 2) + 16 * dg);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+            k[4 * tb + kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + krow + 16 * lg + 64 * kk));
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[4 * tb + i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(vbase[tb] + voff + (D * 2) * i));
+        }
+      }
+      if constexpr (FP8) {
+        // quads 0..3 lie in the first 16 tokens, 4..7 in the second: a per-lane page
+        const char *vp = (tq8 >> 2) ? vbase[1] : vbase[0];
+        const uint32_t voff = (uint32_t)(((ts + 4 * tq8) & (bs - 1)) * D + 16 * dg8);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          v[tb][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + voff + (D * 2) * i));
+          v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + voff + D * i));
       }
     };
 
-    auto compute_tile = [&](int t, const u32x4 (&k)[2][4], u32x4 (&v)[2][4]) {
+    // MFMA A operand of k step kk for token half tb (bf16 pairs)
+    auto k_operand = [&](const u32x4 (&k)[KR], int tb, int kk) -> u32x4 {
+      if constexpr (FP8) {
+        const u32x4 c = k[2 * tb + (kk >> 1)];
+        const uint32_t w0 = (kk & 1) ? c[2] : c[0];
+        const uint32_t w1 = (kk & 1) ? c[3] : c[1];
+        return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                     fp8x2_to_bf16x2<true>(w1)};
+      } else {
+        return k[4 * tb + kk];
+      }
+    };
+
+    auto compute_tile = [&](int t, const u32x4 (&k)[KR], u32x4 (&v)[VR]) {
       const int ts = tok_begin + t * TILE;
       // ---- V^T into this wave's LDS tile (after the previous tile's operand reads) ----
       if (ts + TILE > L) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (ts + 16 * tb + 4 * tqa + i >= L) v[tb][i] = u32x4{0u, 0u, 0u, 0u};
+        for (int r = 0; r < VR; ++r) {
+          const int tok = FP8 ? ts + 4 * tq8 + r : ts + 16 * (r >> 2) + 4 * tqa + (r & 3);
+          if (tok >= L) v[r] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
       wave_lds_fence();
+      if constexpr (FP8) {
+        // byte b of dword w of token i is element 16 dg8 + 4 w + b; gather it over the
+        // four tokens, widen to bf16 and write 8 bytes (4 k slots) of row d
+        const int half = 8 * (tq8 >> 2);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const u32x4 grp = {__builtin_amdgcn_perm(v[0][1][w], v[0][0][w], sel),
-                           __builtin_amdgcn_perm(v[0][3][w], v[0][2][w], sel),
-                           __builtin_amdgcn_perm(v[1][1][w], v[1][0][w], sel),
-                           __builtin_amdgcn_perm(v[1][3][w], v[1][2][w], sel)};
-        *reinterpret_cast<u32x4 *>(vt + vt_offset(8 * dg + e, tqa)) = grp;
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x01 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x05010400u);   // t0b0 t1b0 t0b1 t1b1
+          const uint32_t x23 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x05010400u);
+          const uint32_t y01 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x07030602u);   // t0b2 t1b2 t0b3 t1b3
+          const uint32_t y23 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x07030602u);
+          const int d = 16 * dg8 + 4 * w;
+          *reinterpret_cast<u32x2 *>(vt + vt_offset(d, tq8 & 3) + half) =
+              u32x2{fp8x2_to_bf16x2<false>(x01), fp8x2_to_bf16x2<false>(x23)};
+          *reinterpret_cast<u32x2 *>(vt + vt_offset(d + 1, tq8 & 3) + half) =
+              u32x2{fp8x2_to_bf16x2<true>(x01), fp8x2_to_bf16x2<true>(x23)};
+          *reinterpret_cast<u32x2 *>(vt + vt_offset(d + 2, tq8 & 3) + half) =
+              u32x2{fp8x2_to_bf16x2<false>(y01), fp8x2_to_bf16x2<false>(y23)};
+          *reinterpret_cast<u32x2 *>(vt + vt_offset(d + 3, tq8 & 3) + half) =
+              u32x2{fp8x2_to_bf16x2<true>(y01), fp8x2_to_bf16x2<true>(y23)};
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int w = e >> 1;
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const u32x4 grp = {__builtin_amdgcn_perm(v[1][w], v[0][w], sel),
+                             __builtin_amdgcn_perm(v[3][w], v[2][w], sel),
+                             __builtin_amdgcn_perm(v[5][w], v[4][w], sel),
+                             __builtin_amdgcn_perm(v[7][w], v[6][w], sel)};
+          *reinterpret_cast<u32x4 *>(vt + vt_offset(8 * dg + e, tqa)) = grp;
+        }
       }
       // ---- S^T = K Q^T ----
       f32x4 s[2][NCB];
@@ -313,9 +424,11 @@ void verify_kernel(VerifyLaunch p) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb) {
+          const u32x4 a = k_operand(k, tb, kk);
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) s[tb][cb] = mfma(k[tb][kk], qb[cb][kk], s[tb][cb]);
+          for (int cb = 0; cb < NCB; ++cb) s[tb][cb] = mfma(a, qb[cb][kk], s[tb][cb]);
+        }
       // ---- scale, mask, online softmax per column ----
       const bool masked = ts + TILE - 1 > mask_from;
       float tmax[NCB];
@@ -376,7 +489,7 @@ void verify_kernel(VerifyLaunch p) {
     // (indices past the last tile are clamped to it so every step issues the same loads)
     auto run_tiles = [&](int ta, int tb) {
       const int tl = tb - 1;
-      u32x4 ka[2][4], va[2][4], kb2[2][4], vb2[2][4], kc[2][4], vc[2][4];
+      u32x4 ka[KR], va[VR], kb2[KR], vb2[VR], kc[KR], vc[VR];
       load_tile(ta, ka, va);
       load_tile(min(ta + 1, tl), kb2, vb2);
       for (int t = ta; t < tb; t += 3) {
@@ -409,7 +522,7 @@ void verify_kernel(VerifyLaunch p) {
         const size_t base = ((size_t)(qbase + (c >> log2G)) * Hq + g * G + (c & (G - 1))) * D;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const f32x4 v = o[db][cb];
+          const f32x4 v = o[db][cb] * vscale;
           const float l = lsum[cb];
           store4<OUT_BF16>(p.out, base + 16 * db + 4 * lg, f32x4{v[0] / l, v[1] / l, v[2] / l, v[3] / l});
         }
@@ -417,7 +530,7 @@ void verify_kernel(VerifyLaunch p) {
         const size_t slot = (size_t)(u + worker) * p.slot_cols + c;
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-          *reinterpret_cast<f32x4 *>(p.part_acc + slot * D + 16 * db + 4 * lg) = o[db][cb];
+          *reinterpret_cast<f32x4 *>(p.part_acc + slot * D + 16 * db + 4 * lg) = o[db][cb] * vscale;
         if (lg == 0) {
           p.part_m[slot] = m[cb];
           p.part_l[slot] = lsum[cb];
@@ -425,10 +538,12 @@ void verify_kernel(VerifyLaunch p) {
       }
     }
 
+    }  // cnt > 0
+
     // next unit
-    x += cnt;
-    t0 = 0;
-    ustart += nb;
+    x += cntv;
+    tv = 0;
+    ustart += vnb;
     if (++g == Hkv) {
       g = 0;
       ++rb;
@@ -439,13 +554,14 @@ void verify_kernel(VerifyLaunch p) {
           L = len_of(++rb);
           nb = (L + TILE - 1) / TILE;
         }
+        vnb = nb + C;
       }
     }
   }
 }
 
 // Combine the pieces of one (row, kv head, query column) cut across workers.
-template <bool OUT_BF16>
+template <int ITEM, bool OUT_BF16>
 __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   const int c = blockIdx.x;
   const int u = blockIdx.y;
@@ -455,8 +571,8 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   const int rb = u / Hkv;
   const int g = u % Hkv;
   const int row = p.first_row + rb;
-  const int qbase = p.q_start_loc[row];
-  const int n = p.q_start_loc[row + 1] - qbase;
+  const int qbase = ITEM == kItemDecode ? row : p.q_start_loc[row];
+  const int n = ITEM == kItemDecode ? 1 : p.q_start_loc[row + 1] - qbase;
   if (c >= n * G) return;
   const int cnt = p.seg_count[u];
   if (cnt <= 1) return;                    // written directly by its only worker
@@ -482,31 +598,46 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   }
 }
 
-template <int NCB, bool PREFIX>
-int launch_ncb(const VerifyLaunch &V, hipStream_t st) {
+template <int KV, int ITEM, int NCB>
+int launch_one(const VerifyLaunch &V, hipStream_t st) {
   dim3 grid((V.num_workers + NW - 1) / NW);
   if (V.out_dtype == PA_BF16)
-    hipLaunchKernelGGL((verify_kernel<NCB, true, PREFIX>), grid, dim3(NT), 0, st, V);
+    hipLaunchKernelGGL((verify_kernel<KV, ITEM, NCB, true>), grid, dim3(NT), 0, st, V);
   else
-    hipLaunchKernelGGL((verify_kernel<NCB, false, PREFIX>), grid, dim3(NT), 0, st, V);
+    hipLaunchKernelGGL((verify_kernel<KV, ITEM, NCB, false>), grid, dim3(NT), 0, st, V);
   return (int)hipGetLastError();
+}
+
+template <int KV>
+int launch_kv(const VerifyLaunch &V, hipStream_t st) {
+  const bool wide = V.slot_cols > 16;
+  switch (V.item_kind) {
+    case 0: return wide ? launch_one<KV, kItemVerify, 2>(V, st) : launch_one<KV, kItemVerify, 1>(V, st);
+    case 1: return wide ? launch_one<KV, kItemPrefix, 2>(V, st) : launch_one<KV, kItemPrefix, 1>(V, st);
+    case 2: return wide ? launch_one<KV, kItemDecode, 2>(V, st) : launch_one<KV, kItemDecode, 1>(V, st);
+  }
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace
 
 int launch_verify_partials(const VerifyLaunch &V, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (V.prefix_mode) return V.slot_cols <= 16 ? launch_ncb<1, true>(V, st) : launch_ncb<2, true>(V, st);
-  return V.slot_cols <= 16 ? launch_ncb<1, false>(V, st) : launch_ncb<2, false>(V, st);
+  if (V.kv_dtype == PA_FP8_E4M3) return launch_kv<PA_FP8_E4M3>(V, st);
+  return launch_kv<PA_BF16>(V, st);
 }
 
 int launch_verify_merge(const VerifyLaunch &V, void *stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   dim3 grid(V.slot_cols, V.num_rows * V.num_kv_heads);
-  if (V.out_dtype == PA_BF16)
-    hipLaunchKernelGGL(verify_merge_kernel<true>, grid, dim3(64), 0, st, V);
-  else
-    hipLaunchKernelGGL(verify_merge_kernel<false>, grid, dim3(64), 0, st, V);
+  const bool dec = V.item_kind == 2;
+  if (V.out_dtype == PA_BF16) {
+    if (dec) hipLaunchKernelGGL((verify_merge_kernel<kItemDecode, true>), grid, dim3(64), 0, st, V);
+    else hipLaunchKernelGGL((verify_merge_kernel<kItemVerify, true>), grid, dim3(64), 0, st, V);
+  } else {
+    if (dec) hipLaunchKernelGGL((verify_merge_kernel<kItemDecode, false>), grid, dim3(64), 0, st, V);
+    else hipLaunchKernelGGL((verify_merge_kernel<kItemVerify, false>), grid, dim3(64), 0, st, V);
+  }
   return (int)hipGetLastError();
 }
 

@@ -185,15 +185,17 @@ def test_mixed_verify_class_validation(b, kw, status):
     assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == status
 
 
-def test_mixed_verify_rows_need_bf16_kv(b):
+def test_mixed_verify_rows_take_bf16_or_fp8_kv(b):
     m = _mixed_args(b, num_decode_rows=2, num_verify_rows=2)   # no prefill rows
     m.base.kv_dtype = b.PA_FP8_E4M3
     m.base.k_scale = m.base.v_scale = 0x10000
-    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
-    m.num_verify_rows = 0
-    m.num_decode_rows = 4                                      # FP8 decode rows alone are fine
+    # accepted (it only lacks a workspace)
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_WORKSPACE_TOO_SMALL"
     n = ctypes.c_size_t()
-    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0 and n.value > 0
+    # prefill rows still need a bf16 cache
+    m.num_verify_rows = 1
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
 
 
 def test_mixed_group_bounds_verify_q_len(b):
@@ -420,3 +422,34 @@ def test_append_metadata_checker(b):
 def test_append_struct_layout(b):
     assert b.AppendArgs.k.offset == 32
     assert ctypes.sizeof(b.AppendArgs) == 32 + 7 * 8
+
+
+def test_argument_structs_keep_their_tensors_alive(b):
+    """The C structs carry plain addresses: the builders must hold the tensors they point at.
+
+    A temporary passed inline (out=torch.empty(...)) would otherwise be freed at once and its
+    memory handed to the next allocation while a kernel still writes there.
+    """
+    import gc
+    import torch
+    q = torch.zeros(2, 32, 128, dtype=torch.bfloat16)
+    kp = torch.zeros(4, 8, 16, 128, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    sl = torch.ones(2, dtype=torch.int32)
+    qs = torch.tensor([0, 1, 2], dtype=torch.int32)
+    structs = [
+        b.make_decode_args(q, kp, kp, bt, sl, 0.1, max_seq_len=16, out=torch.empty(2, 32, 128, dtype=torch.bfloat16)),
+        b.make_mixed_args(q, kp, kp, bt, sl, qs, 0.1, num_decode_rows=2, max_q_len=1, max_seq_len=16,
+                          out=torch.empty(2, 32, 128, dtype=torch.bfloat16)),
+        b.make_cascade_args(q, kp, kp, bt, sl, torch.tensor([0, 2], dtype=torch.int32),
+                            torch.zeros(2, dtype=torch.int32), 0.1, max_seq_len=16, max_group_rows=2,
+                            out=torch.empty(2, 32, 128, dtype=torch.bfloat16)),
+    ]
+    gc.collect()
+    for s in structs:
+        out_ptr = s.out if hasattr(s, "out") else s.base.out
+        assert any(t.data_ptr() == out_ptr for t in s._keep)
+    a = b.make_append_args(torch.zeros(3, 8, 128), torch.zeros(3, 8, 128), torch.zeros(3, dtype=torch.int32),
+                           torch.zeros(4, 8, 16, 128), torch.zeros(4, 8, 16, 128))
+    gc.collect()
+    assert any(t.data_ptr() == a.slot_mapping for t in a._keep)
