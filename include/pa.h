@@ -44,7 +44,11 @@
  * pa_mixed_workspace_size).  The library keeps no pointer after a call
  * returns, allocates no memory, and never synchronises: work is queued on
  * `stream` (a hipStream_t; NULL = the default stream) and the call returns.
- * Calls are safe to record into a HIP graph.
+ * pa_mixed runs a batch's prefill-chunk rows on an auxiliary stream beside
+ * its decode and verify rows (event fork and join with `stream`, so all of
+ * the call's work is ordered on `stream` as if queued there); that stream and
+ * two events are created once per device, on first use.  Calls are safe to
+ * record into a HIP graph.
  *
  * Errors.  Every host-checkable problem returns a status before anything is
  * launched: null pointers, misalignment (16 bytes for q, pools, out,

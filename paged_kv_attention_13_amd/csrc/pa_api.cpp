@@ -97,8 +97,32 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
   }
   VerifyLaunch V;
   if (n_ver > 0) make_verify_launch(a, verify_workers, verify_offset, &V);
-  // validation is complete: queue the work
-  if (n_pre > 0) {
+  // validation is complete: queue the work.  Prefill-chunk rows (matrix-core bound) run
+  // on the auxiliary stream beside the decode and verify rows (HBM bound); the decode
+  // kernel is queued first so that it takes its waves before the prefill workgroups.
+  void *pre_stream = stream;
+  const bool fork = n_pre > 0 && (d.num_seqs > 0 || n_ver > 0);
+  if (fork) {
+    s = hip_status(fork_side_stream(stream, &pre_stream), "stream fork");
+    if (s != PA_OK) return s;
+  }
+  pa_status rs = PA_OK;
+  if (d.num_seqs > 0) {
+    if (decode_on_mq(&d)) {
+      VerifyLaunch DV;
+      rs = make_decode_mq_launch(&d, plan, &DV);
+      if (rs == PA_OK) rs = hip_status(launch_verify_partials(DV, stream), "decode");
+      if (rs == PA_OK) rs = hip_status(launch_verify_merge(DV, stream), "merge");
+    } else {
+      rs = hip_status(launch_decode_partials(L, stream), "decode");
+      if (rs == PA_OK) rs = hip_status(launch_merge(L, stream), "merge");
+    }
+  }
+  if (rs == PA_OK && n_ver > 0) {
+    rs = hip_status(launch_verify_partials(V, stream), "verify");
+    if (rs == PA_OK) rs = hip_status(launch_verify_merge(V, stream), "verify merge");
+  }
+  if (rs == PA_OK && n_pre > 0) {
     PrefillLaunch P{};
     P.q = b.q;
     P.k_pool = b.k_pool;
@@ -116,29 +140,13 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.max_q_len = a->max_q_len;
     P.out_dtype = b.out_dtype;
     P.scale = b.scale;
-    s = hip_status(launch_prefill(P, stream), "prefill");
-    if (s != PA_OK) return s;
+    rs = hip_status(launch_prefill(P, pre_stream), "prefill");
   }
-  if (n_ver > 0) {
-    s = hip_status(launch_verify_partials(V, stream), "verify");
-    if (s != PA_OK) return s;
-    s = hip_status(launch_verify_merge(V, stream), "verify merge");
-    if (s != PA_OK) return s;
+  if (fork) {
+    const pa_status js = hip_status(join_side_stream(stream), "stream join");
+    if (rs == PA_OK) rs = js;
   }
-  if (d.num_seqs > 0) {
-    if (decode_on_mq(&d)) {
-      VerifyLaunch DV;
-      s = make_decode_mq_launch(&d, plan, &DV);
-      if (s != PA_OK) return s;
-      s = hip_status(launch_verify_partials(DV, stream), "decode");
-      if (s != PA_OK) return s;
-      return hip_status(launch_verify_merge(DV, stream), "merge");
-    }
-    s = hip_status(launch_decode_partials(L, stream), "decode");
-    if (s != PA_OK) return s;
-    return hip_status(launch_merge(L, stream), "merge");
-  }
-  return PA_OK;
+  return rs;
 }
 
 pa_status pa_decode_cascade(const pa_cascade_args *a, void *stream) {

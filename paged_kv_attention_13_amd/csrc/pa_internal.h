@@ -192,6 +192,10 @@ int launch_append(const AppendLaunch &L, void *stream);
 int launch_verify_partials(const VerifyLaunch &V, void *stream);
 int launch_verify_merge(const VerifyLaunch &V, void *stream);
 int launch_cascade_merge(const CascadeMergeLaunch &M, void *stream);
+// Auxiliary stream of the current device (streams.hip): fork makes it wait for the work
+// queued so far on main_stream; join makes main_stream wait for the work queued on it.
+int fork_side_stream(void *main_stream, void **side_stream);
+int join_side_stream(void *main_stream);
 const char *hip_error_name(int code);
 
 }  // namespace pa

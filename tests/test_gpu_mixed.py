@@ -88,3 +88,47 @@ def test_mixed_full_size_workload():
     ref = oracle.paged_attention_workload(w, rows=rows)
     idx = np.concatenate([np.arange(w.q_start_loc[b], w.q_start_loc[b + 1]) for b in rows])
     compare(got[idx], ref[idx], TOL_BF16, what=f"workload 5 rows {rows}")
+
+
+def test_mixed_graph_replays_match_eager():
+    """A mixed call (decode rows + prefill rows, which fork onto an auxiliary stream and join
+    back) recorded into a graph: every replay equals the eager call, with eager work and a
+    synchronisation between replays."""
+    _announce("mixed call in a graph")
+    import torch
+    from paged_kv_attention_13_amd import binding
+    from paged_kv_attention_13_amd.device import to_device
+    w = _mixed([100, 2000, 5], [(0, 64), (300, 100)], seed=31)
+    d = to_device(w)
+    pre_q = w.q_lens[w.num_decode_rows:]
+    out_e = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    out_g = torch.empty_like(out_e)
+    kw = dict(num_decode_rows=w.num_decode_rows, max_q_len=int(pre_q.max()), max_seq_len=w.max_seq_len)
+    me = binding.make_mixed_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                 d["q_start_loc"], w.scale, out=out_e, **kw)
+    mg = binding.make_mixed_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                 d["q_start_loc"], w.scale, out=out_g, **kw)
+    ws_e = torch.zeros(binding.mixed_workspace_bytes(me), dtype=torch.uint8, device="cuda")
+    ws_g = torch.zeros_like(ws_e)
+    me.base.workspace, me.base.workspace_bytes = ws_e.data_ptr(), ws_e.numel()
+    mg.base.workspace, mg.base.workspace_bytes = ws_g.data_ptr(), ws_g.numel()
+    binding.mixed_args_call(me)
+    torch.cuda.synchronize()
+    ref = oracle.paged_attention_workload(w)
+    compare(out_e.cpu().numpy().astype(np.float64), ref, 5e-3, what="eager mixed")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.mixed_args_call(mg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.mixed_args_call(mg)
+    for rep in range(3):
+        out_g.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        binding.mixed_args_call(me)                      # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), rep
