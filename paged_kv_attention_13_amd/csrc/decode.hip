@@ -156,12 +156,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
     W += __builtin_amdgcn_readlane(incl, 63);
   }
   W *= Hkv;
-  // Planned launches hold two waves per SIMD.  With long work per wave one wave per SIMD
-  // streams HBM a little better (fewer concurrent page streams), so a planned launch
-  // with >= 128 tiles per wave at half the workers uses only the first half: whole
-  // workgroups, one per CU, the rest exit at once.
   int nwk = nworkers;
-  if (p.workers_auto && (nwk % (2 * NW * kTargetCUs)) == 0 && W >= 128LL * (nwk / 2)) nwk /= 2;
   // the plan sized the launch for rows of max_seq_len; shorter rows get fewer, longer ranges
   if (p.workers_auto) nwk = (int)min((long long)nwk, max(1LL, W / p.min_tiles));
   // never more workers than tiles, so that every worker's range is non-empty and the

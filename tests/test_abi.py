@@ -113,12 +113,12 @@ def test_null_struct(b):
 
 
 def test_plan_choices(b):
-    # long context: about as many workers as the chip keeps resident
+    # long context (>= 128 tiles per wave at one wave per SIMD): one worker per SIMD
     a = _args(b, num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192)
     p = b.plan(a)
-    assert p.num_workers == 2048 and p.tile_tokens == 16
+    assert p.num_workers == 1024 and p.tile_tokens == 16
     units = 55 * 8
-    slots = (units + 2048) * 4
+    slots = (units + 1024) * 4
     r256 = lambda x: (x + 255) // 256 * 256
     # (first worker, count) records, then m, l and acc of every partial slot
     assert p.workspace_bytes == r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 512)
@@ -126,6 +126,9 @@ def test_plan_choices(b):
     a.kv_dtype = 2
     a.k_scale = a.v_scale = 0x10000
     assert b.plan(a).tile_tokens == 32
+    # shorter rows: two waves per SIMD, as many as the chip keeps resident
+    a = _args(b, num_seqs=32, block_size=16, max_blocks_per_seq=256, max_seq_len=4096)
+    assert b.plan(a).num_workers == 2048
     # an explicit worker count is honoured
     a = _args(b, num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192, num_workers=7)
     assert b.plan(a).num_workers == 7
