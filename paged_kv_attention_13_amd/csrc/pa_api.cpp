@@ -76,12 +76,12 @@ pa_status pa_append(const pa_append_args *a, void *stream) {
 }
 
 pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
-  pa_decode_args d;
-  pa_plan plan;
-  int verify_workers = 0;
-  size_t verify_offset = 0, total = 0;
-  pa_status s = plan_mixed(a, true, &d, &plan, &verify_workers, &verify_offset, &total);
+  MixedPlan mp;
+  pa_status s = plan_mixed(a, true, &mp);
   if (s != PA_OK) return s;
+  const pa_decode_args &d = mp.dec;
+  const pa_plan &plan = mp.dec_plan;
+  const size_t total = mp.total_bytes;
   const pa_decode_args &b = a->base;
   if (total > 0 && (!b.workspace || b.workspace_bytes < total))
     return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, the batch needs %zu",
@@ -96,7 +96,7 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     if (s != PA_OK) return s;
   }
   VerifyLaunch V;
-  if (n_ver > 0) make_verify_launch(a, verify_workers, verify_offset, &V);
+  if (n_ver > 0) make_verify_launch(a, mp.verify_workers, mp.verify_offset, &V);
   // validation is complete: queue the work.  Prefill-chunk rows (matrix-core bound) run
   // on the auxiliary stream beside the decode and verify rows (HBM bound); the decode
   // kernel is queued first so that it takes its waves before the prefill workgroups.
@@ -140,7 +140,15 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.max_q_len = a->max_q_len;
     P.out_dtype = b.out_dtype;
     P.scale = b.scale;
+    P.splits = mp.prefill_splits;
+    P.max_qtiles = mp.prefill_qtiles;
+    if (mp.prefill_splits > 1) {
+      char *ws = static_cast<char *>(b.workspace);
+      P.part_o = reinterpret_cast<float *>(ws + mp.prefill_offset);
+      P.part_ml = reinterpret_cast<float *>(ws + mp.prefill_ml_offset);
+    }
     rs = hip_status(launch_prefill(P, pre_stream), "prefill");
+    if (rs == PA_OK && mp.prefill_splits > 1) rs = hip_status(launch_prefill_merge(P, pre_stream), "prefill merge");
   }
   if (fork) {
     const pa_status js = hip_status(join_side_stream(stream), "stream join");

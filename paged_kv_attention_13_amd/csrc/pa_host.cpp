@@ -167,9 +167,7 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   return PA_OK;
 }
 
-pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decode_args *dec,
-                     pa_plan *dec_plan, int *verify_workers, size_t *verify_offset,
-                     size_t *total_bytes) {
+pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPlan *mp) {
   if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
   const pa_decode_args &b = a->base;
   pa_status s = validate_decode(&b, need_device_pointers);
@@ -204,6 +202,10 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decod
     if (b.kv_dtype != PA_BF16)
       return set_error(PA_ERR_UNSUPPORTED, "prefill-chunk rows need a bf16 KV cache and bf16 q");
   }
+  pa_decode_args *dec = &mp->dec;
+  pa_plan *dec_plan = &mp->dec_plan;
+  int *verify_workers = &mp->verify_workers;
+  size_t *verify_offset = &mp->verify_offset;
   *dec = b;
   dec->num_seqs = nd;
   plan_decode(dec, dec_plan);
@@ -223,7 +225,39 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decod
     vbytes = round_up(2 * (size_t)units * sizeof(int32_t), 256) + 2 * round_up(slots * sizeof(float), 256) +
              round_up(slots * kHeadDim * sizeof(float), 256);
   }
-  *total_bytes = nv > 0 ? *verify_offset + vbytes : dec_plan->workspace_bytes;
+  size_t total = nv > 0 ? *verify_offset + vbytes : dec_plan->workspace_bytes;
+  // prefill rows: a launch with at most half as many units as resident workgroups
+  // cannot fill the chip, and its units can be long (a chunk after a long cached
+  // prefix), so long units are cut into up to kPrefillMaxSplits kv pieces (of at
+  // least kPrefillMinChunkTiles tiles) whose partials a merge kernel combines.  With
+  // more units the pieces' extra traffic costs more than the balance gains (and in a
+  // mixed batch the prefill already runs hidden beside the decode rows).
+  mp->prefill_splits = 1;
+  mp->prefill_qtiles = 0;
+  mp->prefill_offset = 0;
+  mp->prefill_ml_offset = 0;
+  mp->prefill_slots = 0;
+  if (n_pre > 0) {
+    const int hb = prefill_heads_per_block(G);
+    const int qb = prefill_queries_per_block(G);
+    mp->prefill_qtiles = (a->max_q_len + qb - 1) / qb;
+    const int64_t units_upper = (int64_t)n_pre * b.num_kv_heads * (G / hb) * mp->prefill_qtiles;
+    const int64_t tiles_upper = (b.max_seq_len + kPrefillTile - 1) / kPrefillTile;
+    int splits = 1;
+    if (units_upper <= kPrefillSlots / 2) {
+      splits = (int)std::min<int64_t>(kPrefillMaxSplits, (2 * kPrefillSlots + units_upper - 1) / units_upper);
+      splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, tiles_upper / kPrefillMinChunkTiles));
+    }
+    mp->prefill_splits = splits;
+    if (splits > 1) {
+      mp->prefill_slots = (size_t)units_upper * splits;
+      mp->prefill_offset = round_up(total, 256);
+      mp->prefill_ml_offset =
+          mp->prefill_offset + round_up(mp->prefill_slots * kPrefillWaves * 32 * kHeadDim * sizeof(float), 256);
+      total = mp->prefill_ml_offset + round_up(mp->prefill_slots * kPrefillWaves * 32 * 2 * sizeof(float), 256);
+    }
+  }
+  mp->total_bytes = total;
   return PA_OK;
 }
 
@@ -517,11 +551,9 @@ pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan) {
 
 pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes) {
   if (!a || !bytes) return set_error(PA_ERR_NULL_POINTER, "argument is NULL");
-  pa_decode_args d;
-  pa_plan p;
-  int vw = 0;
-  size_t voff = 0;
-  pa_status s = plan_mixed(a, false, &d, &p, &vw, &voff, bytes);
+  MixedPlan mp;
+  pa_status s = plan_mixed(a, false, &mp);
+  if (s == PA_OK) *bytes = mp.total_bytes;
   return s;
 }
 
@@ -554,11 +586,8 @@ pa_status pa_check_append_metadata(const pa_append_args *a) {
 
 pa_status pa_check_mixed_metadata(const pa_mixed_args *a) {
   if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
-  pa_decode_args d;
-  pa_plan p;
-  int vw = 0;
-  size_t voff = 0, total = 0;
-  pa_status s = plan_mixed(a, false, &d, &p, &vw, &voff, &total);
+  MixedPlan mp;
+  pa_status s = plan_mixed(a, false, &mp);
   if (s != PA_OK) return s;
   const int B = a->base.num_seqs;
   if (B > 0 && (!a->base.seq_lens || !a->base.block_table || !a->q_start_loc))

@@ -27,6 +27,16 @@ constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
 constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
 constexpr int kVerifyMaxWorkers = kTargetCUs * 4;   // one verify wave per SIMD
 constexpr int kMqUnitCost = 4;           // multi-query kernel: start-up cost of a unit, in tiles
+constexpr int kPrefillTile = 64;         // prefill kernel: kv tokens per tile
+constexpr int kPrefillSlots = kTargetCUs * 2;   // prefill workgroups resident at once (2 per CU)
+constexpr int kPrefillMaxSplits = 4;     // prefill: at most this many kv pieces per unit
+constexpr int kPrefillMinChunkTiles = 4; // prefill: a piece covers at least this many tiles
+constexpr int kPrefillWaves = 4;         // prefill: waves per workgroup, 32 query positions each
+
+// Prefill geometry for group size G: query heads per workgroup (HB) and query
+// positions per workgroup (QB); a unit is (row, kv head, head block, query tile).
+inline int prefill_heads_per_block(int G) { return G == 1 ? 1 : (G == 2 ? 2 : 4); }
+inline int prefill_queries_per_block(int G) { return 32 * (kPrefillWaves / prefill_heads_per_block(G)); }
 
 // Everything a decode launch needs, resolved on the host.
 struct DecodeLaunch {
@@ -76,6 +86,13 @@ struct PrefillLaunch {
   int max_q_len;
   int out_dtype;
   float scale;
+  // kv split of long units: every unit's tiles are cut into pieces of C tiles
+  // (C computed in the kernel from the rows' lengths, at least ceil(tiles / splits));
+  // pieces of a cut unit go to per-(unit, piece) slots and a merge kernel combines them
+  int splits;                    // 1 = no split
+  int max_qtiles;                // ceil(max_q_len / QB)
+  float *part_o;                 // [slot][4 waves][32 q][128] fp32, unnormalised
+  float *part_ml;                // [slot][4 waves][32 q][2] fp32: running max (log2 domain), sum
 };
 
 struct VerifyLaunch {
@@ -163,11 +180,23 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan);
 pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, DecodeLaunch *L);
 pa_status validate_append(const pa_append_args *a, bool need_device_pointers);
 size_t elem_bytes(int dtype);
-// Checks the pa_mixed row classes; fills the decode and verify sub-plans and the
-// total workspace size (decode part first, then the verify part at verify_offset).
-pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, pa_decode_args *dec,
-                     pa_plan *dec_plan, int *verify_workers, size_t *verify_offset,
-                     size_t *total_bytes);
+// Sub-plans of a pa_mixed call: decode rows, verify rows, prefill rows.  Workspace:
+// decode part first, then the verify part at verify_offset, then the prefill
+// pieces at prefill_offset (only when prefill_splits > 1).
+struct MixedPlan {
+  pa_decode_args dec;
+  pa_plan dec_plan;
+  int verify_workers = 0;
+  size_t verify_offset = 0;
+  int prefill_splits = 1;
+  int prefill_qtiles = 0;
+  size_t prefill_offset = 0;      // piece outputs
+  size_t prefill_ml_offset = 0;   // piece (max, sum) pairs
+  size_t prefill_slots = 0;
+  size_t total_bytes = 0;
+};
+// Checks the pa_mixed row classes and fills the plan.
+pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPlan *mp);
 pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_offset,
                              VerifyLaunch *V);
 // Decode rows whose pools are FP8 run on the multi-query kernel (one query column per
@@ -190,6 +219,7 @@ int tile_tokens(int kv_dtype);
 int launch_decode_partials(const DecodeLaunch &L, void *stream);
 int launch_merge(const DecodeLaunch &L, void *stream);
 int launch_prefill(const PrefillLaunch &L, void *stream);
+int launch_prefill_merge(const PrefillLaunch &L, void *stream);
 int launch_append(const AppendLaunch &L, void *stream);
 int launch_verify_partials(const VerifyLaunch &V, void *stream);
 int launch_verify_merge(const VerifyLaunch &V, void *stream);

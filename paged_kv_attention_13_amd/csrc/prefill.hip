@@ -22,9 +22,12 @@
 // 8-byte LDS stores.  Per tile and wave:
 //   S^T = K Q^T   : 32 x v_mfma_f32_16x16x32_bf16  (A = K rows from LDS,
 //                   B = Q^T held in registers for the whole row)
-//   online softmax in fp32 (log2 domain, lazy rescale as in the decode kernel)
+//   online softmax in fp32 (log2 domain, lazy rescale as in the decode kernel;
+//                   the scale folded into one fused multiply-add per weight)
 //   O^T += V^T P^T: 32 x v_mfma_f32_16x16x32_bf16  (A = V^T from LDS,
 //                   B = P^T straight from the S^T accumulators)
+//   denominators  : v_dot2_f32_bf16 of each packed weight pair with (1, 1), so the
+//                   sum takes the same bf16 weights as the product
 // Computing S transposed puts each lane's probabilities exactly where the
 // B operand of the second product wants them (same lane, same query
 // column), so no cross-lane transpose is needed: within one 32-token k step
@@ -74,6 +77,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// c + lo(w) + hi(w) for a packed bf16 pair w (products by 1.0 are exact)
+__device__ __forceinline__ float dot2_ones(uint32_t w, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), c,
+                                         false);
+}
+
 template <bool OUT_BF16>
 __device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
   if constexpr (OUT_BF16) {
@@ -82,6 +91,36 @@ __device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
   } else {
     *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + idx) = v;
   }
+}
+
+// Piece length (in kv tiles) of a split launch, the same in every wave of the prefill
+// kernel and of its merge: at least ceil(longest row's tiles / splits), so the launch's
+// `splits` pieces per unit always cover the unit, and at least 1.25 x the average work
+// per resident workgroup, so that a launch whose units are already balanced is not cut
+// further.  The work estimate per row takes its query tiles' mean visible length.
+template <int QB>
+__device__ int piece_tiles(const PrefillLaunch &p, int lane, int units_per_qtile) {
+  if (p.splits <= 1) return 1 << 30;
+  int mx = 0;
+  int64_t work = 0;                        // tile visits, x 2 (half tiles are counted)
+  for (int r0 = 0; r0 < p.num_rows; r0 += 64) {
+    const int r = p.first_row + r0 + lane;
+    if (r0 + lane < p.num_rows) {
+      const int L = p.seq_lens[r];
+      const int n = p.q_start_loc[r + 1] - p.q_start_loc[r];
+      const int nq = (n + QB - 1) / QB;
+      mx = max(mx, (L + KT - 1) / KT);
+      work += (int64_t)nq * ((2 * (int64_t)(L - n) + n + QB) / KT + 2);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mx = max(mx, __shfl_xor(mx, off));
+    work += __shfl_xor(work, off);
+  }
+  const int64_t total = work * units_per_qtile / 2;
+  const int balanced = (int)((5 * total + 4 * kPrefillSlots - 1) / (4 * kPrefillSlots));
+  return max(max((mx + p.splits - 1) / p.splits, balanced), kPrefillMinChunkTiles);
 }
 
 // HB: query heads per workgroup (1, 2 or 4); the 4 waves cover HB heads x (4/HB) query sub-tiles.
@@ -100,10 +139,15 @@ void prefill_kernel(PrefillLaunch p) {
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int hblocks = G / HB;              // head blocks per kv head
-  const int qt = blockIdx.x;
+  // x: query tile, the longest (last in the row) dispatched first; z: (piece, row) with the
+  // piece slowest, so consecutive workgroups (spread round-robin over the XCDs) are
+  // different units rather than pieces of one unit that may have no work
+  const int qt = p.max_qtiles - 1 - (int)blockIdx.x;
+  const int piece = (int)blockIdx.z / p.num_rows;
+  const int row_local = (int)blockIdx.z % p.num_rows;
   const int g = blockIdx.y / hblocks;
   const int hb = blockIdx.y % hblocks;
-  const int row = p.first_row + blockIdx.z;
+  const int row = p.first_row + row_local;
   const int q_begin = p.q_start_loc[row];
   const int n = p.q_start_loc[row + 1] - q_begin;
   if (qt * QB >= n) return;                // whole workgroup: past this row's chunk
@@ -118,8 +162,14 @@ void prefill_kernel(PrefillLaunch p) {
   const int h = g * G + hb * HB + (wave % HB);
   const int q0 = qt * QB + (wave / HB) * QW;              // first query of this wave
   const int blk_last_q = min(qt * QB + QB, n) - 1;
-  const int kv_end = prior + blk_last_q + 1;              // tokens the workgroup visits
+  const int kv_end = prior + blk_last_q + 1;              // tokens the unit visits
   const int ntile = (kv_end + KT - 1) / KT;
+  // this workgroup's piece of the unit: tiles [j_begin, j_end)
+  const int C = __builtin_amdgcn_readfirstlane(piece_tiles<QB>(p, tid & 63, Hkv * hblocks));
+  const int j_begin = piece * C;
+  if (j_begin >= ntile) return;            // whole workgroup: the unit has fewer pieces
+  const int j_end = min(ntile, j_begin + C);
+  const bool split = ntile > C;
   const int wave_last_pos = prior + min(q0 + QW, n) - 1;  // last position among this wave's queries
   const bool wave_active = q0 < n;
 
@@ -156,10 +206,11 @@ void prefill_kernel(PrefillLaunch p) {
   // stage the block-table entries of every page the loads below can touch in LDS, so the
   // pipelined loads depend on one LDS read instead of a global load.  The loads cover
   // every token < L of the workgroup's tiles, which can run past kv_end in the last tile.
-  const int npages = (min(L, ntile * KT) + bs - 1) >> log2bs;
+  const int page0 = (j_begin * KT) >> log2bs;
+  const int npages = ((min(L, j_end * KT) + bs - 1) >> log2bs) - page0;
   const bool tbl_in_lds = npages <= kTblLds;
   if (tbl_in_lds)
-    for (int i = tid; i < npages; i += NTP) s_tbl[i] = trow[i];
+    for (int i = tid; i < npages; i += NTP) s_tbl[i] = trow[page0 + i];
   __syncthreads();
 
   u32x4 rk[CHUNKS], rv[CHUNKS];
@@ -168,7 +219,7 @@ void prefill_kernel(PrefillLaunch p) {
     const int t_first = j * KT + 4 * c_tq;
     const bool any = t_first < L;
     const int page = t_first >> log2bs;
-    const int phys = !any ? 0 : (tbl_in_lds ? s_tbl[page] : trow[page]);
+    const int phys = !any ? 0 : (tbl_in_lds ? s_tbl[page - page0] : trow[page]);
     const size_t base = (size_t)phys * phys_stride + (size_t)(t_first & (bs - 1)) * D + 8 * c_dg;
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
@@ -201,13 +252,13 @@ void prefill_kernel(PrefillLaunch p) {
     }
   };
 
-  float m[2] = {kNegBig, kNegBig};
-  float lsum[2] = {0.f, 0.f};              // per-lane partial of the softmax denominator
+  float m[2] = {kNegBig, kNegBig};        // running max of the scaled logits (log2 units)
   f32x4 o[8][2];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum[2] = {0.f, 0.f};              // per-lane partial of the softmax denominator
 
   auto compute = [&](int j) {
     const char *kb = s_k[j & 1];
@@ -240,29 +291,32 @@ void prefill_kernel(PrefillLaunch p) {
         for (int qt2 = 0; qt2 < 2; ++qt2) s[tt][qt2] = mfma(ka[ks & 1][tt], qb[qt2][ks], s[tt][qt2]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- scale, causal mask, online softmax (per query column) ----
+    // ---- causal mask, online softmax (per query column) ----
+    // the max is taken over the raw scores (the scale is positive) and the scale enters each
+    // weight through one fused multiply-add: p = 2^(s * scale * log2(e) - m)
     const bool diag = kv0 + KT - 1 > prior + q0;          // some element may be masked
     float tmax[2];
 #pragma unroll
     for (int qt2 = 0; qt2 < 2; ++qt2) {
       const int qi = q0 + 16 * qt2 + lq;
       const int pos = prior + min(qi, n - 1);
+      if (diag) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = kv0 + 16 * tt + 4 * lg + i;
+            s[tt][qt2][i] = tok <= pos ? s[tt][qt2][i] : -__builtin_inff();
+          }
+      }
       float mx = -__builtin_inff();
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[tt][qt2][i] * qk_scale;
-          if (diag) {
-            const int tok = kv0 + 16 * tt + 4 * lg + i;
-            x = tok <= pos ? x : -__builtin_inff();
-          }
-          s[tt][qt2][i] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][qt2][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      tmax[qt2] = mx;
+      tmax[qt2] = mx * qk_scale;
     }
     const bool need = tmax[0] > m[0] + kSlack || tmax[1] > m[1] + kSlack;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -285,17 +339,14 @@ void prefill_kernel(PrefillLaunch p) {
         float pv[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = fast_exp2(s[2 * ks2][qt2][i] - m[qt2]);
-          pv[4 + i] = fast_exp2(s[2 * ks2 + 1][qt2][i] - m[qt2]);
+          pv[i] = fast_exp2(__builtin_fmaf(s[2 * ks2][qt2][i], qk_scale, -m[qt2]));
+          pv[4 + i] = fast_exp2(__builtin_fmaf(s[2 * ks2 + 1][qt2][i], qk_scale, -m[qt2]));
         }
         pb[qt2][ks2] = u32x4{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                              pack_bf16(pv[6], pv[7])};
         // the denominator sums the same bf16-rounded weights the product uses
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t pw = pb[qt2][ks2][w];
-          lsum[qt2] += __builtin_bit_cast(float, pw << 16) + __builtin_bit_cast(float, pw & 0xFFFF0000u);
-        }
+        for (int w = 0; w < 4; ++w) lsum[qt2] = dot2_ones(pb[qt2][ks2][w], lsum[qt2]);
       }
     // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -316,15 +367,15 @@ void prefill_kernel(PrefillLaunch p) {
 
   // pipeline: tile j is computed from LDS while tile j+1 waits in LDS and tile j+2's
   // global loads are in flight; one barrier per tile
-  load_regs(0);
-  store_lds(0);
-  if (ntile > 1) load_regs(1);
+  load_regs(j_begin);
+  store_lds(j_begin & 1);
+  if (j_begin + 1 < j_end) load_regs(j_begin + 1);
   __syncthreads();
-  for (int j = 0; j < ntile; ++j) {
+  for (int j = j_begin; j < j_end; ++j) {
     if (wave_active && j * KT <= wave_last_pos) compute(j);   // else fully masked for this wave
-    if (j + 1 < ntile) {
+    if (j + 1 < j_end) {
       store_lds((j + 1) & 1);
-      if (j + 2 < ntile) load_regs(j + 2);
+      if (j + 2 < j_end) load_regs(j + 2);
     }
     __syncthreads();
   }
@@ -335,6 +386,25 @@ void prefill_kernel(PrefillLaunch p) {
   for (int qt2 = 0; qt2 < 2; ++qt2) {
     lsum[qt2] += __shfl_xor(lsum[qt2], 16);
     lsum[qt2] += __shfl_xor(lsum[qt2], 32);
+  }
+  if (split) {
+    // a piece of a cut unit: the unnormalised sum, the running max and the sum of
+    // weights go to the piece's slot (a wave that saw no tile of this piece leaves
+    // max = -1e30, sum = 0, zeros); the merge kernel combines the pieces
+    const size_t slot = ((((size_t)row_local * gridDim.y + blockIdx.y) * p.max_qtiles + qt) * p.splits +
+                         piece) * NWP + wave;
+    float *po = p.part_o + slot * (QW * D);
+    float *pml = p.part_ml + slot * (QW * 2);
+#pragma unroll
+    for (int qt2 = 0; qt2 < 2; ++qt2) {
+      const int ql = 16 * qt2 + lq;
+      if (q0 + ql >= n) continue;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4 *>(po + ql * D + 16 * dt + 4 * lg) = o[dt][qt2];
+      if (lg == 0) *reinterpret_cast<float2 *>(pml + 2 * ql) = float2{m[qt2], lsum[qt2]};
+    }
+    return;
   }
 #pragma unroll
   for (int qt2 = 0; qt2 < 2; ++qt2) {
@@ -350,15 +420,118 @@ void prefill_kernel(PrefillLaunch p) {
   }
 }
 
+// Merge of the pieces of every cut unit (same grid as the prefill kernel without the
+// piece index): out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p with M = max_p m_p,
+// the rescaling identity of the online softmax applied across pieces.  x = (query tile,
+// quarter): a workgroup merges 8 of the 32 query positions of each of the unit's waves,
+// so four times as many workgroups keep loads in flight.  Lane c < 8 of a wave first
+// forms the normalised piece weights of its c-th position; then lane pairs take one
+// position each, 4 consecutive head-dim elements per lane, all four steps unrolled.
+template <int HB, bool OUT_BF16>
+__global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
+  constexpr int QSUB = NWP / HB;
+  constexpr int QB = QW * QSUB;
+  const int Hq = p.num_q_heads;
+  const int Hkv = p.num_kv_heads;
+  const int G = Hq / Hkv;
+  const int hblocks = G / HB;
+  constexpr int QM = QW / 4;               // positions per wave and workgroup
+  const int qt = p.max_qtiles - 1 - (int)blockIdx.x / 4;
+  const int quarter = (int)blockIdx.x % 4;
+  const int g = blockIdx.y / hblocks;
+  const int hb = blockIdx.y % hblocks;
+  const int row = p.first_row + blockIdx.z;
+  const int q_begin = p.q_start_loc[row];
+  const int n = p.q_start_loc[row + 1] - q_begin;
+  if (qt * QB >= n) return;
+  const int L = p.seq_lens[row];
+  const int prior = L - n;
+  const int ntile = (prior + min(qt * QB + QB, n) + KT - 1) / KT;
+  const int tid = threadIdx.x;
+  const int C = __builtin_amdgcn_readfirstlane(piece_tiles<QB>(p, tid & 63, Hkv * hblocks));
+  if (ntile <= C) return;                  // the prefill kernel stored this unit itself
+  const int npieces = (ntile + C - 1) / C;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = g * G + hb * HB + (wave % HB);
+  const int q0 = qt * QB + (wave / HB) * QW;
+  if (q0 >= n) return;
+  const int qm0 = quarter * QM;            // first position (within the wave's 32) merged here
+  const int q_lim = min(QW, n - q0);
+  if (qm0 >= q_lim) return;
+  const size_t slot0 = ((((size_t)blockIdx.z * gridDim.y + blockIdx.y) * p.max_qtiles + qt) * p.splits) * NWP + wave;
+  const float *__restrict__ po = p.part_o + slot0 * (QW * D);
+  const float *__restrict__ pml = p.part_ml + slot0 * (QW * 2);
+  constexpr size_t kPieceO = (size_t)NWP * QW * D;       // floats between pieces of one slot
+  constexpr size_t kPieceML = (size_t)NWP * QW * 2;
+  float wt[kPrefillMaxSplits];
+  {
+    const int c = qm0 + (lane & (QM - 1));
+    float mp[kPrefillMaxSplits], lp[kPrefillMaxSplits];
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int s = 0; s < kPrefillMaxSplits; ++s) {
+      mp[s] = -__builtin_inff();
+      lp[s] = 0.f;
+      if (s < npieces && c < q_lim) {
+        const float2 ml = *reinterpret_cast<const float2 *>(pml + s * kPieceML + 2 * c);
+        mp[s] = ml.x;
+        lp[s] = ml.y;
+      }
+      M = fmaxf(M, mp[s]);
+    }
+    float den = 0.f;
+#pragma unroll
+    for (int s = 0; s < kPrefillMaxSplits; ++s) {
+      wt[s] = s < npieces && c < q_lim ? fast_exp2(mp[s] - M) : 0.f;
+      den += wt[s] * lp[s];
+    }
+#pragma unroll
+    for (int s = 0; s < kPrefillMaxSplits; ++s) wt[s] = c < q_lim ? wt[s] / den : 0.f;
+  }
+  const int half = lane >> 5;
+  const int d = 4 * (lane & 31);
+#pragma unroll
+  for (int qq = 0; qq < QM; qq += 2) {
+    const int ql = qm0 + qq + half;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kPrefillMaxSplits; ++s) {
+      const float w = __shfl(wt[s], qq + half);
+      if (s < npieces && ql < q_lim)
+        acc += w * *reinterpret_cast<const f32x4 *>(po + s * kPieceO + ql * D + d);
+    }
+    if (ql < q_lim) store4<OUT_BF16>(p.out, ((size_t)(q_begin + q0 + ql) * Hq + h) * D + d, acc);
+  }
+}
+
 template <int HB>
 int launch_hb(const PrefillLaunch &P, hipStream_t st) {
   constexpr int QB = QW * (NWP / HB);
   const int G = P.num_q_heads / P.num_kv_heads;
-  dim3 grid((P.max_q_len + QB - 1) / QB, P.num_kv_heads * (G / HB), P.num_rows);
+  if (P.max_qtiles != (P.max_q_len + QB - 1) / QB || P.splits < 1 || P.splits > kPrefillMaxSplits ||
+      (P.splits > 1 && (!P.part_o || !P.part_ml)))
+    return (int)hipErrorInvalidValue;
+  dim3 grid(P.max_qtiles, P.num_kv_heads * (G / HB), P.num_rows * P.splits);
   if (P.out_dtype == PA_BF16)
     hipLaunchKernelGGL((prefill_kernel<HB, true>), grid, dim3(NTP), 0, st, P);
   else
     hipLaunchKernelGGL((prefill_kernel<HB, false>), grid, dim3(NTP), 0, st, P);
+  return (int)hipGetLastError();
+}
+
+template <int HB>
+int launch_merge_hb(const PrefillLaunch &P, hipStream_t st) {
+  constexpr int QB = QW * (NWP / HB);
+  const int G = P.num_q_heads / P.num_kv_heads;
+  if (P.max_qtiles != (P.max_q_len + QB - 1) / QB || P.splits < 2 || P.splits > kPrefillMaxSplits ||
+      !P.part_o || !P.part_ml)
+    return (int)hipErrorInvalidValue;
+  dim3 grid(P.max_qtiles * 4, P.num_kv_heads * (G / HB), P.num_rows);
+  if (P.out_dtype == PA_BF16)
+    hipLaunchKernelGGL((prefill_merge_kernel<HB, true>), grid, dim3(NTP), 0, st, P);
+  else
+    hipLaunchKernelGGL((prefill_merge_kernel<HB, false>), grid, dim3(NTP), 0, st, P);
   return (int)hipGetLastError();
 }
 
@@ -372,6 +545,18 @@ int launch_prefill(const PrefillLaunch &P, void *stream) {
     case 2: return launch_hb<2>(P, st);
     case 4: return launch_hb<4>(P, st);
     case 8: return launch_hb<4>(P, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+int launch_prefill_merge(const PrefillLaunch &P, void *stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int G = P.num_q_heads / P.num_kv_heads;
+  switch (G) {
+    case 1: return launch_merge_hb<1>(P, st);
+    case 2: return launch_merge_hb<2>(P, st);
+    case 4: return launch_merge_hb<4>(P, st);
+    case 8: return launch_merge_hb<4>(P, st);
   }
   return (int)hipErrorInvalidValue;
 }

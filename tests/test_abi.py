@@ -241,6 +241,29 @@ def test_mixed_workspace_holds_verify_partials(b):
     assert n2.value == r256(n3.value) + r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 512)
 
 
+def test_mixed_workspace_holds_prefill_pieces(b):
+    """Prefill rows with fewer units than resident workgroups get kv pieces: one slot of
+    4 waves x 32 queries x (128 + 2) fp32 per (unit, piece); with many units, none."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    m = _mixed_args(b, num_verify_rows=0)                     # 1 decode row + 3 prefill rows
+    m.base.max_blocks_per_seq, m.base.max_seq_len = 256, 4096
+    n = ctypes.c_size_t()
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    dec = b.plan(_args(b, num_seqs=1, max_blocks_per_seq=256, max_seq_len=4096)).workspace_bytes
+    units = 3 * 8 * 1 * 1          # rows x kv heads x head blocks (group 4) x query tiles of 32
+    splits = min(4, -(-2 * 512 // units), max(1, (4096 // 64) // 4))
+    assert splits == 4
+    slots = units * splits
+    assert n.value == r256(dec) + r256(slots * 4 * 32 * 128 * 4) + r256(slots * 4 * 32 * 2 * 4)
+    m.max_q_len = 4096                                        # 3 x 8 x 128 units > 512
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    assert n.value == dec
+    m.max_q_len = 8
+    m.base.max_seq_len = 128                                  # 2 tiles: pieces would be too short
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    assert n.value == b.plan(_args(b, num_seqs=1, max_blocks_per_seq=256, max_seq_len=128)).workspace_bytes
+
+
 def _cascade_args(b, **kw):
     c = b.CascadeArgs()
     c.base = _args(b, num_seqs=4, max_seq_len=128)

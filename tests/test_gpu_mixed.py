@@ -78,6 +78,37 @@ def test_prefill_constant_v_exact():
     np.testing.assert_array_equal(got, 2.0)
 
 
+def test_prefill_split_matches_unsplit():
+    """Few units: long units are cut into kv pieces and merged.  The same rows with a
+    max_q_len bound large enough to fill the chip run unsplit; both match the oracle and
+    each other (only the order of the sums differs)."""
+    _announce("prefill pieces vs one pass")
+    w = _mixed([], [(3000, 64), (0, 200), (1500, 33), (40, 1)], seed=41)
+    ref = oracle.paged_attention_workload(w)
+    got_split = run_mixed(w, out_dtype="f32")
+    compare(got_split, ref, 1e-2, what="prefill in pieces")
+    import torch
+    from paged_kv_attention_13_amd import binding
+    from paged_kv_attention_13_amd.device import to_device
+    d = to_device(w)
+    out = binding.mixed(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], d["q_start_loc"],
+                        w.scale, num_decode_rows=0, max_q_len=1024, max_seq_len=w.max_seq_len, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got_one = out.cpu().numpy().astype(np.float64)
+    compare(got_one, ref, 1e-2, what="prefill in one pass")
+    assert np.max(np.abs(got_one - got_split)) <= 2e-3
+
+
+def test_prefill_many_units_unsplit():
+    """More units than resident workgroups: no kv split, longest query tiles first."""
+    _announce("prefill, 3 rows x 1024 new tokens")
+    w = _mixed([7], [(500, 1024), (0, 1024), (2000, 1000)], seed=43)
+    got = run_mixed(w)
+    rows = [0, 1, 2, 3]
+    ref = oracle.paged_attention_workload(w, rows=rows)
+    compare(got, ref, TOL_BF16, what="3 x 1024 prefill")
+
+
 def test_mixed_full_size_workload():
     _announce(f"workload 5: {pa_inputs.WORKLOAD_NAMES[5]}")
     w = pa_inputs.make_config(5)
