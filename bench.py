@@ -44,7 +44,10 @@ def parse():
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
     ap.add_argument("--loop-batch", type=int, default=1,
                     help="--op loop: decode rows in the steady batch")
-    ap.add_argument("--op", default="decode", choices=["decode", "append", "append-fp8", "cascade", "loop"],
+    ap.add_argument("--prefill-case", default="w5-rows",
+                    help="--op prefill: w5-rows, chunk256-after8192 or prompt8192")
+    ap.add_argument("--op", default="decode",
+                    choices=["decode", "append", "append-fp8", "cascade", "loop", "prefill"],
                     help="decode: the attention call of --workload (default); append / append-fp8: "
                          "writing the mixed workload's 2,144 new tokens (96 decode + 8 x 256 prefill) "
                          "into their cache slots, bf16 -> bf16 or bf16 -> FP8-E4M3; cascade: the "
@@ -264,6 +267,43 @@ def bench_cascade(args):
     }), flush=True)
 
 
+def bench_prefill(args):
+    """Causal prefill-chunk rows alone (pa_mixed with no decode or verify rows)."""
+    import torch
+
+    import pa_inputs
+    from paged_kv_attention_13_amd import accounting, binding
+    from paged_kv_attention_13_amd.device import to_device
+
+    w = pa_inputs.make_prefill_case(args.prefill_case)
+    d = to_device(w)
+    out = torch.empty(d["q"].shape, dtype=torch.bfloat16, device="cuda")
+    m = binding.make_mixed_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"],
+                                d["q_start_loc"], w.scale, num_decode_rows=0, max_q_len=int(w.q_lens.max()),
+                                max_seq_len=w.max_seq_len, out=out)
+    ws = torch.empty(max(binding.mixed_workspace_bytes(m), 16), dtype=torch.uint8, device="cuda")
+    m.base.workspace, m.base.workspace_bytes = ws.data_ptr(), ws.numel()
+    c_ms, wall = _timed(lambda: binding.mixed_args_call(m), args.steps, args.warmup)
+    flops = accounting.call_flops(w.seq_lens, w.q_lens, w.num_q_heads, w.head_dim)
+    ach = flops / (c_ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "prefill-chunk attention: algorithmic TFLOP/s (causal part only)",
+        "value": round(flops / (wall * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values)",
+        "config": {"workload": w.name, "rows": w.num_seqs, "new_tokens": int(w.q_lens.sum()),
+                   "cached_tokens": int(w.seq_lens.sum()), "block_size": w.block_size,
+                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim},
+        "flops_per_call": int(flops),
+        "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "pa_mixed call (prefill kernel, plus the piece merge when units are few)",
+                     "kernel_ms_mean": round(c_ms, 5)},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
 def bench_loop(args):
     """Decode steps of a 32-layer attention stack at small batch: eager launches vs one graph replay."""
     import numpy as np
@@ -351,6 +391,9 @@ def main():
         return
     if args.op == "loop":
         bench_loop(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
     if args.op != "decode":
         bench_append(args)

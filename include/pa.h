@@ -215,7 +215,10 @@ int pa_abi_version(void);
  * (2 x int32), then (units + workers) partial slots of Hq/Hkv x (128 + 2) fp32. */
 pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
 
-/* Workspace bytes a pa_mixed call needs (its decode rows' split-K partials). */
+/* Workspace bytes a pa_mixed call needs: its decode rows' split-K partials, its
+ * verify rows' partials and, when the prefill rows make at most 256 (row, kv
+ * head, head block, 32- to 128-position query tile) units, their kv pieces:
+ * up to 4 per unit, each 4 x 32 x (128 + 2) fp32. */
 pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes);
 
 /* Decode attention over the paged cache: the decode kernel followed by the
@@ -240,7 +243,9 @@ pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
  * verify rows through the split-K MFMA multi-query kernels (bf16 q and KV),
  * prefill-chunk rows through the MFMA causal tile kernel (bf16 q and KV), all
  * on `stream`.  The workspace (pa_mixed_workspace_size) holds the decode rows'
- * split records and partials followed by the verify rows'. */
+ * split records and partials, then the verify rows', then the prefill pieces
+ * (a launch of few units cuts long units' cached context into up to 4 pieces
+ * and a merge kernel, also on the prefill stream, combines them). */
 pa_status pa_mixed(const pa_mixed_args *a, void *stream);
 
 /* Shared-prefix decode: the prefix kernel (one pass over each group's shared

@@ -392,6 +392,28 @@ def workload_lengths(i: int, seed: Optional[int] = None):
     raise ValueError(i)
 
 
+# prefill-only cases (bf16, 32 q / 8 kv heads, 16-token blocks): (seq_lens, q_lens)
+PREFILL_CASES = {
+    # workload 5's eight prefill-chunk rows alone (its seeded lengths)
+    "w5-rows": None,
+    # one chunk of 256 new tokens after 8,192 cached ones (few units: the kv-piece path)
+    "chunk256-after8192": ([8192 + 256], [256]),
+    # one 8,192-token prompt from scratch (many units)
+    "prompt8192": ([8192], [8192]),
+}
+
+
+def make_prefill_case(name: str, seed: int = 2024) -> Workload:
+    """A prefill-only workload named in PREFILL_CASES."""
+    if name == "w5-rows":
+        L, ql = workload_lengths(5)
+        nd = leading_decode_rows(ql)
+        L, ql = L[nd:], ql[nd:]
+    else:
+        L, ql = PREFILL_CASES[name]
+    return make_workload(name=f"prefill {name}", seq_lens=L, q_lens=ql, block_size=16, seed=seed)
+
+
 def make_config(i: int, seed: Optional[int] = None, poison_unused: bool = False) -> Workload:
     """Named workload i (1..7) at full size."""
     seed = (1000 + i) if seed is None else seed
