@@ -112,3 +112,18 @@ def test_small_workload_is_small():
     w = pa_inputs.make_config(1)
     assert w.k_pool.shape == (32, 8, 16, 128) and w.k_pool.dtype == np.float32
     assert sorted(w.block_table[0].tolist()) == list(range(32))
+
+
+def test_prefill_cases_flops():
+    """The prefill-only cases: 4*D*Hq per (query, visible key) pair, causal part only."""
+    import pa_inputs
+    from paged_kv_attention_13_amd import accounting
+    w = pa_inputs.make_prefill_case("prompt8192")
+    assert accounting.call_flops(w.seq_lens, w.q_lens, 32, 128) == 4 * 128 * 32 * (8192 * 8193 // 2)
+    w = pa_inputs.make_prefill_case("chunk256-after8192")
+    assert accounting.call_flops(w.seq_lens, w.q_lens, 32, 128) == 4 * 128 * 32 * (256 * 8192 + 256 * 257 // 2)
+    w = pa_inputs.make_prefill_case("w5-rows")
+    w5 = pa_inputs.make_config(5)
+    nd = w5.num_decode_rows
+    assert list(w.seq_lens) == list(w5.seq_lens[nd:]) and list(w.q_lens) == list(w5.q_lens[nd:])
+    assert accounting.call_flops(w.seq_lens, w.q_lens, 32, 128) == 31151095808
