@@ -260,6 +260,11 @@ void prefill_kernel(PrefillLaunch p) {
     for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = f32x4{0.f, 0.f, 0.f, 0.f};
   float lsum[2] = {0.f, 0.f};              // per-lane partial of the softmax denominator
 
+  // lane parts of the V^T operand addresses (see the product below)
+  const int vt_lane = lq * V_STRIDE + 8 * ((lg & 1) ^ (lq >> 3));
+  const int vt_lane_even = vt_lane + 16 * ((lg >> 1) & 1);
+  const int vt_lane_odd = vt_lane + 16 * (((lg >> 1) & 1) ^ 1);
+
   auto compute = [&](int j) {
     const char *kb = s_k[j & 1];
     const char *vb = s_vt[j & 1];
@@ -314,14 +319,17 @@ void prefill_kernel(PrefillLaunch p) {
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][qt2][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      tmax[qt2] = mx * qk_scale;
+      tmax[qt2] = mx * qk_scale;           // this lane's part of the column max
     }
+    // A column needs rescaling when its max exceeds m by more than the slack, i.e. when
+    // one of its lanes' parts does: the vote needs no cross-lane reduction, which the
+    // rare rescale path then does (same values as reducing first)
     const bool need = tmax[0] > m[0] + kSlack || tmax[1] > m[1] + kSlack;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int qt2 = 0; qt2 < 2; ++qt2) {
+        tmax[qt2] = fmaxf(tmax[qt2], __shfl_xor(tmax[qt2], 16));
+        tmax[qt2] = fmaxf(tmax[qt2], __shfl_xor(tmax[qt2], 32));
         const float mn = fmaxf(m[qt2], tmax[qt2]);
         const float a = fast_exp2(m[qt2] - mn);
         m[qt2] = mn;
@@ -353,11 +361,13 @@ void prefill_kernel(PrefillLaunch p) {
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int vr = 16 * dt + lq;                 // row d of V^T; groups swizzled by d >> 3
-        const int sw = (vr >> 3) & 15;
-        const char *vrow = vb + vr * V_STRIDE;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 8 * ((8 * ks2 + lg) ^ sw));
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 8 * ((8 * ks2 + 4 + lg) ^ sw));
+        // row d = 16 dt + lq of V^T, groups (8 ks2 + 4 half + lg) ^ (d >> 3): the XOR splits
+        // into bits, so the address is a lane base (two variants, by dt's parity) plus an
+        // immediate -- no per-read address arithmetic
+        const char *vrow = vb + ((dt & 1) ? vt_lane_odd : vt_lane_even) + 16 * dt * V_STRIDE;
+        const int g_hi = 8 * (8 * (ks2 ^ ((dt >> 2) & 1)));
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + g_hi + 8 * 4 * ((dt >> 1) & 1));
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + g_hi + 8 * 4 * (((dt >> 1) & 1) ^ 1));
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = mfma(a, pb[qt2][ks2], o[dt][qt2]);
@@ -411,11 +421,19 @@ void prefill_kernel(PrefillLaunch p) {
     const int qi = q0 + 16 * qt2 + lq;
     if (qi >= n) continue;
     const size_t base = ((size_t)(q_begin + qi) * Hq + h) * D;
+    // o / l as o * (1/l) with one residual correction (l >= 1: the running max is at most
+    // 8 below the column's max, so no special values); o = c * l gives exactly c
+    const float l = lsum[qt2];
+    const float r = __builtin_amdgcn_rcpf(l);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const f32x4 v = o[dt][qt2];
-      const f32x4 r = {v[0] / lsum[qt2], v[1] / lsum[qt2], v[2] / lsum[qt2], v[3] / lsum[qt2]};
-      store4<OUT_BF16>(p.out, base + 16 * dt + 4 * lg, r);
+      f32x4 v = o[dt][qt2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q = v[i] * r;
+        v[i] = __builtin_fmaf(__builtin_fmaf(-l, q, v[i]), r, q);
+      }
+      store4<OUT_BF16>(p.out, base + 16 * dt + 4 * lg, v);
     }
   }
 }

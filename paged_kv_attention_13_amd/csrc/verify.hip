@@ -444,16 +444,18 @@ void verify_kernel(VerifyLaunch p) {
             s[tb][cb][i] = xv;
             mx = fmaxf(mx, xv);
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        tmax[cb] = mx;
+        tmax[cb] = mx;                     // this lane's part of the column max
       }
+      // a column needs rescaling when one of its lanes' parts exceeds m by more than the
+      // slack: the vote needs no cross-lane reduction, which the rare rescale path does
       bool need = false;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) need |= tmax[cb] > m[cb] + kSlack;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
+          tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 16));
+          tmax[cb] = fmaxf(tmax[cb], __shfl_xor(tmax[cb], 32));
           const float mn = fmaxf(m[cb], tmax[cb]);
           const float a = fast_exp2(m[cb] - mn);
           m[cb] = mn;
