@@ -25,7 +25,7 @@ def _mixed(dec_lens, pre, bs=16, hq=32, hkv=8, seed=0, poison=True):
 PRE = [(0, 1), (0, 5), (0, 64), (3, 29), (17, 33), (100, 64), (250, 130), (0, 256), (1000, 96)]
 
 
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
 def test_mixed_ragged(bs):
     _announce(f"mixed ragged bs={bs}")
     w = _mixed([1, 40, 700, 3000], PRE, bs=bs, seed=bs)
@@ -97,6 +97,16 @@ def test_prefill_split_matches_unsplit():
     got_one = out.cpu().numpy().astype(np.float64)
     compare(got_one, ref, 1e-2, what="prefill in one pass")
     assert np.max(np.abs(got_one - got_split)) <= 2e-3
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_prefill_pieces_start_mid_page(bs):
+    """Pieces of 64-token tiles over 128-token pages start in the middle of a page."""
+    _announce(f"prefill pieces, bs={bs}")
+    w = _mixed([], [(5000, 40), (700, 300)], bs=bs, seed=47 + bs)
+    ref = oracle.paged_attention_workload(w)
+    got = run_mixed(w, out_dtype="f32")
+    compare(got, ref, 1e-2, what=f"prefill pieces bs{bs}")
 
 
 def test_prefill_many_units_unsplit():
