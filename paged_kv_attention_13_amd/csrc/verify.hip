@@ -487,19 +487,19 @@ void verify_kernel(VerifyLaunch p) {
       }
     };
 
-    // software pipeline over tiles [ta, tb): three register sets, two tiles in flight
-    // (indices past the last tile are clamped to it so every step issues the same loads)
+    // software pipeline over tiles [ta, tb): three register sets, two tiles in flight;
+    // look-ahead loads past the last tile are skipped (loading the last tile again
+    // would fetch it from HBM again: the loads do not allocate in the caches)
     auto run_tiles = [&](int ta, int tb) {
-      const int tl = tb - 1;
       u32x4 ka[KR], va[VR], kb2[KR], vb2[VR], kc[KR], vc[VR];
       load_tile(ta, ka, va);
-      load_tile(min(ta + 1, tl), kb2, vb2);
+      if (ta + 1 < tb) load_tile(ta + 1, kb2, vb2);
       for (int t = ta; t < tb; t += 3) {
-        load_tile(min(t + 2, tl), kc, vc);
+        if (t + 2 < tb) load_tile(t + 2, kc, vc);
         compute_tile(t, ka, va);
-        load_tile(min(t + 3, tl), ka, va);
+        if (t + 3 < tb) load_tile(t + 3, ka, va);
         if (t + 1 < tb) compute_tile(t + 1, kb2, vb2);
-        load_tile(min(t + 4, tl), kb2, vb2);
+        if (t + 4 < tb) load_tile(t + 4, kb2, vb2);
         if (t + 2 < tb) compute_tile(t + 2, kc, vc);
       }
     };
