@@ -397,31 +397,30 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
     };
 
     // Software pipeline over tiles [ta, tb) with NBUF register sets: while one tile
-    // is computed, the next NBUF-1 tiles are in flight.  Tile indices past the last
-    // are clamped to it (an L2-resident reload) so every step issues the same loads
-    // and the wait counts stay static.  Nothing else is loaded inside the pipeline:
-    // a conditional load there would make the compiler drain every load before each
-    // use of the block-table register.
+    // is computed, the next NBUF-1 tiles are in flight.  Look-ahead loads past the
+    // last tile are skipped: the loads do not allocate in the caches, so re-loading
+    // the last tile would fetch it from HBM again.  Nothing else is loaded inside the
+    // pipeline: a load there would make the compiler drain every load before each use
+    // of the block-table register.
     auto run_tiles = [&](int ta, int tb) {
-      const int tl = tb - 1;
       u32x4 ka[TPL][EB], va[TPL][EB], kb[TPL][EB], vb[TPL][EB];
       load_tile(ta, ka, va);
       if constexpr (NBUF == 3) {
         u32x4 kc[TPL][EB], vc[TPL][EB];
-        load_tile(min(ta + 1, tl), kb, vb);
+        if (ta + 1 < tb) load_tile(ta + 1, kb, vb);
         for (int t = ta; t < tb; t += 3) {
-          load_tile(min(t + 2, tl), kc, vc);
+          if (t + 2 < tb) load_tile(t + 2, kc, vc);
           compute_tile(t, ka, va);
-          load_tile(min(t + 3, tl), ka, va);
+          if (t + 3 < tb) load_tile(t + 3, ka, va);
           if (t + 1 < tb) compute_tile(t + 1, kb, vb);
-          load_tile(min(t + 4, tl), kb, vb);
+          if (t + 4 < tb) load_tile(t + 4, kb, vb);
           if (t + 2 < tb) compute_tile(t + 2, kc, vc);
         }
       } else {
         for (int t = ta; t < tb; t += 2) {
-          load_tile(min(t + 1, tl), kb, vb);
+          if (t + 1 < tb) load_tile(t + 1, kb, vb);
           compute_tile(t, ka, va);
-          load_tile(min(t + 2, tl), ka, va);
+          if (t + 2 < tb) load_tile(t + 2, ka, va);
           if (t + 1 < tb) compute_tile(t + 1, kb, vb);
         }
       }
