@@ -525,8 +525,303 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch p) {
   store_out<OUT_BF16>(p.out, o + 1, n1 / den);
 }
 
+// Short rows (at most 64 pages and kUnitMaxTokens tokens, as bounded by max_seq_len):
+// one workgroup per (row, kv head) unit.  Its 8 (or 4) waves take consecutive shares of
+// the unit's tiles and then combine their (max, sum, output) states in LDS with the same
+// log-sum-exp identity as the merge kernel, so there is no workspace and no second
+// launch.  The row's length, its block-table entries (all within the first 64) and
+// its queries do not depend on each other, so they are loaded together before any
+// KV load.  Per-tile arithmetic as in decode_kernel.
+template <int KV, int G, bool OUT_BF16>
+__global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(DecodeLaunch p) {
+  constexpr int NWU = unit_waves(KV, G);   // waves per workgroup
+  constexpr int NTU = NWU * 64;
+  constexpr int EB = KvTraits<KV>::EB;
+  constexpr int TPL = KvTraits<KV>::TPL;
+  constexpr int TILE = 8 * TPL;
+  constexpr int DW = 4 * EB;
+  constexpr bool kBf = KV != PA_F32;
+  constexpr int NBUF = (KV == PA_F32 || G >= 8) ? 2 : 3;
+  __shared__ float s_ml[NWU][G][2];
+  __shared__ float s_acc[NWU][G][D];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Hq = p.num_q_heads;
+  const int Hkv = p.num_kv_heads;
+  const int b = blockIdx.x / Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int c = lane & 7;
+  const int grp = lane >> 3;
+
+  // independent loads first
+  const int L = p.seq_lens[b];
+  const int tbl = p.block_table[(size_t)b * p.max_blocks_per_seq + min(lane, p.max_blocks_per_seq - 1)];
+  uint32_t qb[G][8];
+  float qf[G][16];
+  if constexpr (kBf) {
+    const uint16_t *q = static_cast<const uint16_t *>(p.q) + ((size_t)b * Hq + g * G) * D;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        qb[hh][i] = *reinterpret_cast<const uint32_t *>(q + hh * D + elem_d<EB>(c, 2 * i));
+  } else {
+    const float *q = static_cast<const float *>(p.q) + ((size_t)b * Hq + g * G) * D;
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qf[hh][e] = q[hh * D + elem_d<EB>(c, e)];
+  }
+
+  const int nb = (L + TILE - 1) / TILE;
+  const int t_lo = wave * nb / NWU;
+  const int t_hi = (wave + 1) * nb / NWU;
+  const int bs = p.block_size;
+  const int log2bs = __builtin_ctz(bs);
+  const size_t page_bytes = (size_t)bs * D * EB;
+  const size_t phys_stride = (size_t)Hkv * page_bytes;
+  const int lane_off = c * 16;
+  const float qk_scale = p.scale * kLog2e;
+  const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
+  const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
+
+  float m[G], l[G], acc[G][16];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    m[hh] = kNegBig;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[hh][e] = 0.f;
+  }
+
+  if (t_hi > t_lo) {
+    const int tok_begin = t_lo * TILE;
+    const int tok_end = min(t_hi * TILE, L);
+    const int last_page = (tok_end - 1) >> log2bs;
+
+    auto load_tile = [&](int t, u32x4 (&k)[TPL][EB], u32x4 (&v)[TPL][EB]) {
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        const int tok0 = tok_begin + t * TILE + 8 * r;
+        const int page = min(tok0 >> log2bs, last_page);
+        const int phys = __builtin_amdgcn_readlane(tbl, page);
+        const char *kp = kpool + (size_t)phys * phys_stride;
+        const char *vp = vpool + (size_t)phys * phys_stride;
+        const uint32_t off = (uint32_t)(((tok0 + grp) & (bs - 1)) * (D * EB) + lane_off);
+#pragma unroll
+        for (int j = 0; j < EB; ++j) {
+          k[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + off + j * 128));
+          v[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + off + j * 128));
+        }
+      }
+    };
+
+    auto compute_tile = [&](int t, const u32x4 (&k)[TPL][EB], u32x4 (&v)[TPL][EB]) {
+      const int tile_start = tok_begin + t * TILE;
+      float sc[TPL][G];
+#pragma unroll
+      for (int r = 0; r < TPL; ++r) {
+        uint32_t kd[DW];
+#pragma unroll
+        for (int i = 0; i < DW; ++i) kd[i] = k[r][i / 4][i % 4];
+        if constexpr (kBf) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = dot2bf(qb[hh][i], kd[i], a);
+            sc[r][hh] = a;
+          }
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) a = __builtin_fmaf(qf[hh][e], __builtin_bit_cast(float, kd[e]), a);
+            sc[r][hh] = a;
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < TPL; ++r)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          float y = sc[r][hh];
+          y += dpp<kDppXor1>(y);
+          y += dpp<kDppXor2>(y);
+          y += dpp<kDppHalfMirror>(y);
+          sc[r][hh] = y * qk_scale;
+        }
+      if (tile_start + TILE > tok_end) {
+#pragma unroll
+        for (int r = 0; r < TPL; ++r) {
+          if (tile_start + 8 * r + grp >= tok_end) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) sc[r][hh] = -__builtin_inff();
+#pragma unroll
+            for (int j = 0; j < EB; ++j) v[r][j] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+      float tmax[G];
+      bool need = false;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float y = sc[0][hh];
+#pragma unroll
+        for (int r = 1; r < TPL; ++r) y = fmaxf(y, sc[r][hh]);
+        tmax[hh] = y;
+        need |= y > m[hh] + kSlack;
+      }
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float mn = fmaxf(m[hh], tmax[hh]);
+          const float a = fast_exp2(m[hh] - mn);
+          m[hh] = mn;
+          l[hh] *= a;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[hh][e] *= a;
+        }
+      }
+      float pr[TPL][G];
+#pragma unroll
+      for (int r = 0; r < TPL; ++r)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) pr[r][hh] = fast_exp2(sc[r][hh] - m[hh]);
+      if constexpr (kBf) {
+        constexpr uint32_t kOnes = 0x3F803F80u;
+#pragma unroll
+        for (int w2 = 0; w2 < TPL / 2; ++w2) {
+          const int r0 = 2 * w2, r1 = 2 * w2 + 1;
+          uint32_t pp[G];
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            pp[hh] = pack_bf16(pr[r0][hh], pr[r1][hh]);
+            l[hh] = dot2bf(pp[hh], kOnes, l[hh]);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t A = v[r0][i / 4][i % 4];
+            const uint32_t Bv = v[r1][i / 4][i % 4];
+            const uint32_t lo = __builtin_amdgcn_perm(Bv, A, 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(Bv, A, 0x07060302u);
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+              acc[hh][2 * i] = dot2bf(lo, pp[hh], acc[hh][2 * i]);
+              acc[hh][2 * i + 1] = dot2bf(hi, pp[hh], acc[hh][2 * i + 1]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < TPL; ++r) {
+          float vf[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const uint32_t bits = v[r][e / 4][e % 4];
+            vf[e] = __builtin_bit_cast(float, bits);
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            l[hh] += pr[r][hh];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[hh][e] = __builtin_fmaf(pr[r][hh], vf[e], acc[hh][e]);
+          }
+        }
+      }
+    };
+
+    const int cnt = t_hi - t_lo;
+    u32x4 ka[TPL][EB], va[TPL][EB], kb[TPL][EB], vb[TPL][EB];
+    load_tile(0, ka, va);
+    if constexpr (NBUF == 3) {
+      u32x4 kc[TPL][EB], vc[TPL][EB];
+      if (1 < cnt) load_tile(1, kb, vb);
+      for (int t = 0; t < cnt; t += 3) {
+        if (t + 2 < cnt) load_tile(t + 2, kc, vc);
+        compute_tile(t, ka, va);
+        if (t + 3 < cnt) load_tile(t + 3, ka, va);
+        if (t + 1 < cnt) compute_tile(t + 1, kb, vb);
+        if (t + 4 < cnt) load_tile(t + 4, kb, vb);
+        if (t + 2 < cnt) compute_tile(t + 2, kc, vc);
+      }
+    } else {
+      for (int t = 0; t < cnt; t += 2) {
+        if (t + 1 < cnt) load_tile(t + 1, kb, vb);
+        compute_tile(t, ka, va);
+        if (t + 2 < cnt) load_tile(t + 2, ka, va);
+        if (t + 1 < cnt) compute_tile(t + 1, kb, vb);
+      }
+    }
+
+    // merge the 8 token groups of the wave
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float M = m[hh];
+      M = fmaxf(M, dpp<kDppRowRor8>(M));
+      M = fmaxf(M, __shfl_xor(M, 16));
+      M = fmaxf(M, __shfl_xor(M, 32));
+      const float a = fast_exp2(m[hh] - M);
+      m[hh] = M;
+      float lv = l[hh] * a;
+      lv += dpp<kDppRowRor8>(lv);
+      lv += __shfl_xor(lv, 16);
+      lv += __shfl_xor(lv, 32);
+      l[hh] = lv;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float y = acc[hh][e] * a;
+        y += dpp<kDppRowRor8>(y);
+        y += __shfl_xor(y, 16);
+        y += __shfl_xor(y, 32);
+        acc[hh][e] = y;
+      }
+    }
+  }
+
+  // every wave (one with no tiles holds max -1e30, sum 0, zeros) publishes its state;
+  // token group hh writes head hh
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    if (grp != hh) continue;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s_acc[wave][hh][elem_d<EB>(c, e)] = acc[hh][e];
+    if (c == 0) {
+      s_ml[wave][hh][0] = m[hh];
+      s_ml[wave][hh][1] = l[hh];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += NTU) {
+    const int hh = i / D;
+    const int d = i % D;
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < NWU; ++w) M = fmaxf(M, s_ml[w][hh][0]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWU; ++w) {
+      const float wt = fast_exp2(s_ml[w][hh][0] - M);
+      den = __builtin_fmaf(wt, s_ml[w][hh][1], den);
+      num = __builtin_fmaf(wt, s_acc[w][hh][d], num);
+    }
+    store_out<OUT_BF16>(p.out, ((size_t)b * Hq + g * G + hh) * D + d, num / den);
+  }
+}
+
 template <int KV, int G>
 int launch_kv_g(const DecodeLaunch &L, hipStream_t st) {
+  if (L.unit_mode) {
+    if (L.kv_start) return (int)hipErrorInvalidValue;
+    dim3 ugrid((unsigned)L.num_seqs * L.num_kv_heads);
+    if (L.out_dtype == PA_BF16)
+      hipLaunchKernelGGL((decode_unit_kernel<KV, G, true>), ugrid, dim3(unit_waves(KV, G) * 64), 0, st, L);
+    else
+      hipLaunchKernelGGL((decode_unit_kernel<KV, G, false>), ugrid, dim3(unit_waves(KV, G) * 64), 0, st, L);
+    return (int)hipGetLastError();
+  }
   dim3 grid((L.num_workers + NW - 1) / NW);
   if constexpr (KV == PA_BF16) {
     if (L.kv_start) {
@@ -567,6 +862,7 @@ int launch_decode_partials(const DecodeLaunch &L, void *stream) {
 }
 
 int launch_merge(const DecodeLaunch &L, void *stream) {
+  if (L.unit_mode) return 0;               // the unit kernel wrote every output itself
   hipStream_t st = static_cast<hipStream_t>(stream);
   dim3 grid(L.num_q_heads, L.num_seqs);
   if (L.out_dtype == PA_BF16)

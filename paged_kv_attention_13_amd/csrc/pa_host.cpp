@@ -116,7 +116,12 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
   }
   plan->num_workers = nw;
   plan->tile_tokens = tile;
-  if (a->num_seqs == 0) {
+  if (decode_unit_mode(a)) {
+    // one workgroup of 8 (or 4) waves per (row, kv head) unit, merged in LDS
+    const int waves = unit_waves(a->kv_dtype, a->num_q_heads / a->num_kv_heads);
+    plan->num_workers = (int32_t)std::min<int64_t>((int64_t)a->num_seqs * a->num_kv_heads * waves, INT32_MAX);
+    plan->workspace_bytes = 0;
+  } else if (a->num_seqs == 0) {
     plan->workspace_bytes = 0;
   } else {
     const size_t units = (size_t)a->num_seqs * a->num_kv_heads;
@@ -148,7 +153,8 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   L->kv_dtype = a->kv_dtype;
   L->out_dtype = a->out_dtype;
   L->scale = a->scale;
-  if (a->num_seqs > 0) {
+  L->unit_mode = decode_unit_mode(a);
+  if (a->num_seqs > 0 && !L->unit_mode) {
     if (!a->workspace || a->workspace_bytes < plan.workspace_bytes)
       return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, plan needs %zu",
                        a->workspace ? a->workspace_bytes : (size_t)0, plan.workspace_bytes);

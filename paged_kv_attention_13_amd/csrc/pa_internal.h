@@ -27,6 +27,11 @@ constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
 constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
 constexpr int kVerifyMaxWorkers = kTargetCUs * 4;   // one verify wave per SIMD
 constexpr int kMqUnitCost = 4;           // multi-query kernel: start-up cost of a unit, in tiles
+constexpr int kUnitMaxTokens = 1024;     // decode: rows bounded by this many tokens (and 64
+                                         // pages) run one workgroup per (row, kv head) unit
+// waves of that workgroup: 8, or 4 where the per-wave state is large (fp32 pools,
+// or 8 query heads per kv head), which then fits one wave per SIMD without spills
+constexpr int unit_waves(int kv_dtype, int group) { return (kv_dtype == PA_F32 || group >= 8) ? 4 : 8; }
 constexpr int kPrefillTile = 64;         // prefill kernel: kv tokens per tile
 constexpr int kPrefillSlots = kTargetCUs * 2;   // prefill workgroups resident at once (2 per CU)
 constexpr int kPrefillMaxSplits = 4;     // prefill: at most this many kv pieces per unit
@@ -67,6 +72,7 @@ struct DecodeLaunch {
   int kv_dtype;
   int out_dtype;
   float scale;
+  int unit_mode;       // 1: one workgroup per (row, kv head) unit, no workspace, no merge
 };
 
 struct PrefillLaunch {
@@ -203,6 +209,12 @@ pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_
 // head); this builds that launch over the decode workspace layout.
 pa_status make_decode_mq_launch(const pa_decode_args *a, const pa_plan &plan, VerifyLaunch *V);
 inline bool decode_on_mq(const pa_decode_args *a) { return a->kv_dtype == PA_FP8_E4M3; }
+// Short rows with the worker count left to the library: one workgroup per unit
+// (every row within the first 64 block-table entries and kUnitMaxTokens tokens).
+inline bool decode_unit_mode(const pa_decode_args *a) {
+  return a->num_workers == 0 && a->num_seqs > 0 && a->kv_dtype != PA_FP8_E4M3 &&
+         a->max_seq_len <= kUnitMaxTokens && a->max_seq_len <= 64 * a->block_size;
+}
 // Resident multi-query waves: one per SIMD, two for FP8 pools with <= 16 columns.
 inline int mq_max_workers(int kv_dtype, int slot_cols) {
   return (kv_dtype == PA_FP8_E4M3 && slot_cols <= 16) ? 2 * kVerifyMaxWorkers : kVerifyMaxWorkers;

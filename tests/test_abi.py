@@ -94,7 +94,7 @@ BAD = [
     (dict(k_pool=0x10004), "PA_ERR_MISALIGNED"),
     (dict(num_workers=-1), "PA_ERR_UNSUPPORTED"),
     (dict(num_workers=70000), "PA_ERR_UNSUPPORTED"),
-    (dict(max_seq_len=1000, max_blocks_per_seq=64), "PA_ERR_WORKSPACE_TOO_SMALL"),
+    (dict(max_seq_len=2000, max_blocks_per_seq=128), "PA_ERR_WORKSPACE_TOO_SMALL"),
 ]
 
 
@@ -132,10 +132,19 @@ def test_plan_choices(b):
     # an explicit worker count is honoured
     a = _args(b, num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192, num_workers=7)
     assert b.plan(a).num_workers == 7
-    # tiny work: fewer workers, at least a few tiles each
-    a = _args(b, num_seqs=1, max_seq_len=512, max_blocks_per_seq=32)
+    # tiny work with an explicit split: fewer workers, at least a few tiles each
+    a = _args(b, num_seqs=1, max_seq_len=2048, max_blocks_per_seq=128)
     p = b.plan(a)
-    assert p.num_workers == 8 * 32 // 4
+    assert p.num_workers == 8 * 128 // 4
+    # rows within 1,024 tokens: one workgroup of 8 waves per (row, kv head), no workspace
+    a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
+    p = b.plan(a)
+    assert p.num_workers == 3 * 8 * 8 and p.workspace_bytes == 0
+    a.num_workers = 5                                         # an explicit count keeps the split
+    assert b.plan(a).num_workers == 5 and b.plan(a).workspace_bytes > 0
+    a.num_workers = 0
+    a.kv_dtype, a.k_scale, a.v_scale = 2, 0x10000, 0x10000   # FP8 runs on the multi-query kernel
+    assert b.plan(a).workspace_bytes > 0
     # no rows: no workspace
     a = _args(b, num_seqs=0)
     assert b.plan(a).workspace_bytes == 0

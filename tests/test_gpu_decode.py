@@ -179,6 +179,35 @@ def test_split_invariance():
         assert np.max(np.abs(o - outs[0])) <= 8e-3
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8)])
+def test_short_rows_one_workgroup_per_unit(hq, hkv):
+    """Rows within 1,024 tokens with the worker count left to the library run one workgroup
+    per (row, kv head), its waves merged in LDS (no workspace); they match the oracle and
+    the balanced split of the same rows."""
+    _announce(f"one workgroup per unit, hq={hq} hkv={hkv}")
+    from paged_kv_attention_13_amd import binding
+    w = _small([1, 15, 16, 17, 48, 63, 300, 1000, 1024], hq=hq, hkv=hkv, seed=60 + hq)
+    a = binding.DecodeArgs()
+    a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = w.num_seqs, hq, hkv, 128
+    a.block_size, a.num_blocks, a.max_blocks_per_seq = w.block_size, w.num_blocks, w.max_blocks_per_seq
+    a.max_seq_len, a.q_dtype, a.kv_dtype, a.out_dtype = w.max_seq_len, 1, 1, 1
+    assert binding.plan(a).workspace_bytes == 0
+    ref = oracle.paged_attention_workload(w)
+    unit = run_decode(w, out_dtype="f32")
+    split = run_decode(w, out_dtype="f32", num_workers=37)
+    compare(unit, ref, 5e-3, what="one workgroup per unit")
+    compare(split, ref, 5e-3, what="split")
+    assert np.max(np.abs(unit - split)) <= 8e-3
+
+
+def test_short_rows_constant_v_exact():
+    _announce("one workgroup per unit, constant V")
+    w = _small([1, 40, 1000, 7], seed=71)
+    w.v_pool[...] = np.uint16(0x4000)       # 2.0
+    pa_inputs.poison_pool(w)
+    np.testing.assert_array_equal(run_decode(w, out_dtype="f32"), 2.0)
+
+
 def test_many_workers_more_than_tiles():
     """More workers than tiles: surplus workers find an empty range and exit."""
     _announce("surplus workers")
