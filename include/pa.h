@@ -264,6 +264,21 @@ pa_status pa_check_cascade_metadata(const pa_cascade_args *a_host);
 pa_status pa_append(const pa_append_args *a, void *stream);
 pa_status pa_check_append_metadata(const pa_append_args *a_host);
 
+/* A decode step's append and attention together: the same results as
+ * pa_append(app) followed by pa_decode(dec) on `stream`.  Token b of `app` is
+ * decode row b's newest token: num_tokens == num_seqs, the two argument sets
+ * describe the same pools, and slot_mapping[b] is -1 or the slot of position
+ * seq_lens[b] - 1 of row b (pa_check_append_decode_metadata verifies this on
+ * host copies).  When the decode plan runs one workgroup per (row, kv head)
+ * (rows within 1,024 tokens, worker count left to the library, fp32 or bf16
+ * pools) this is one launch: each workgroup writes its row's new K/V to the
+ * slot and takes position seq_len - 1 from the new rows rather than from the
+ * slot, so no part of the launch reads memory it writes.  Otherwise the two
+ * calls are queued one after the other.  For a decode loop whose layers each
+ * append one token and attend (one launch per layer instead of two). */
+pa_status pa_append_decode(const pa_append_args *app, const pa_decode_args *dec, void *stream);
+pa_status pa_check_append_decode_metadata(const pa_append_args *app_host, const pa_decode_args *dec_host);
+
 /* Synchronous CPU validation of the metadata preconditions above.  The
  * pointers block_table, seq_lens (and q_start_loc) must be HOST pointers;
  * q/pool/out pointers are not read. */

@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: 
 EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_decode",
             "pa_decode_partials", "pa_merge_partials", "pa_mixed", "pa_append", "pa_check_decode_metadata",
             "pa_check_mixed_metadata", "pa_check_append_metadata", "pa_cascade_workspace_size",
-            "pa_decode_cascade", "pa_check_cascade_metadata", "pa_status_string", "pa_last_error"]
+            "pa_decode_cascade", "pa_check_cascade_metadata", "pa_append_decode",
+            "pa_check_append_decode_metadata", "pa_status_string", "pa_last_error"]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -121,6 +122,8 @@ def _load():
         "pa_mixed": ([P(MixedArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_append": ([P(AppendArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_check_append_metadata": ([P(AppendArgs)], ctypes.c_int),
+        "pa_append_decode": ([P(AppendArgs), P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_check_append_decode_metadata": ([P(AppendArgs), P(DecodeArgs)], ctypes.c_int),
         "pa_check_decode_metadata": ([P(DecodeArgs)], ctypes.c_int),
         "pa_check_mixed_metadata": ([P(MixedArgs)], ctypes.c_int),
         "pa_cascade_workspace_size": ([P(CascadeArgs), P(ctypes.c_size_t)], ctypes.c_int),
@@ -442,6 +445,11 @@ def make_append_args(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=N
     a.k_scale = _ptr(k_scale)
     a.v_scale = _ptr(v_scale)
     return _hold(a, k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale)
+
+
+def append_decode_args_call(app: AppendArgs, dec: DecodeArgs, stream=None) -> None:
+    """``pa_append_decode``: append each decode row's new token, then attend (one launch for short rows)."""
+    check(LIB.pa_append_decode(ctypes.byref(app), ctypes.byref(dec), ctypes.c_void_p(_stream(stream))))
 
 
 def append(k, v, slot_mapping, k_pool, v_pool, k_scale=None, v_scale=None, stream=None) -> None:

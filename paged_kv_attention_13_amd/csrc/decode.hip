@@ -532,7 +532,10 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch p) {
 // launch.  The row's length, its block-table entries (all within the first 64) and
 // its queries do not depend on each other, so they are loaded together before any
 // KV load.  Per-tile arithmetic as in decode_kernel.
-template <int KV, int G, bool OUT_BF16>
+// APPEND: also append row b's new token (its K/V rows k_new/v_new[b]) at slot
+// new_slots[b] and take position L - 1 from those rows instead of the pool: nothing in
+// this launch reads the slot being written, and the values are the ones the slot gets.
+template <int KV, int G, bool OUT_BF16, bool APPEND>
 __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(DecodeLaunch p) {
   constexpr int NWU = unit_waves(KV, G);   // waves per workgroup
   constexpr int NTU = NWU * 64;
@@ -574,6 +577,16 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
       for (int e = 0; e < 16; ++e) qf[hh][e] = q[hh * D + elem_d<EB>(c, e)];
   }
 
+  int new_slot = -1;
+  const char *knew = nullptr;
+  const char *vnew = nullptr;
+  if constexpr (APPEND) {
+    new_slot = p.new_slots[b];
+    const size_t row_off = ((size_t)b * Hkv + g) * D * EB;
+    knew = static_cast<const char *>(p.k_new) + row_off;
+    vnew = static_cast<const char *>(p.v_new) + row_off;
+  }
+
   const int nb = (L + TILE - 1) / TILE;
   const int t_lo = wave * nb / NWU;
   const int t_hi = (wave + 1) * nb / NWU;
@@ -585,6 +598,17 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
   const float qk_scale = p.scale * kLog2e;
   const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
   const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
+  if constexpr (APPEND) {
+    // the appended row: 16 bytes per lane of wave 0
+    if (wave == 0 && new_slot >= 0 && lane < D * EB / 16) {
+      const size_t dst = (size_t)(new_slot >> log2bs) * phys_stride + (size_t)g * page_bytes +
+                         (size_t)(new_slot & (bs - 1)) * (D * EB) + 16 * lane;
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(p.k_pool_w) + dst) =
+          *reinterpret_cast<const u32x4 *>(knew + 16 * lane);
+      *reinterpret_cast<u32x4 *>(static_cast<char *>(p.v_pool_w) + dst) =
+          *reinterpret_cast<const u32x4 *>(vnew + 16 * lane);
+    }
+  }
 
   float m[G], l[G], acc[G][16];
 #pragma unroll
@@ -609,10 +633,18 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
         const char *kp = kpool + (size_t)phys * phys_stride;
         const char *vp = vpool + (size_t)phys * phys_stride;
         const uint32_t off = (uint32_t)(((tok0 + grp) & (bs - 1)) * (D * EB) + lane_off);
+        const char *ka = kp + off;
+        const char *va = vp + off;
+        if constexpr (APPEND) {
+          if (new_slot >= 0 && tok0 + grp == L - 1) {
+            ka = knew + lane_off;
+            va = vnew + lane_off;
+          }
+        }
 #pragma unroll
         for (int j = 0; j < EB; ++j) {
-          k[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(kp + off + j * 128));
-          v[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + off + j * 128));
+          k[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ka + j * 128));
+          v[r][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(va + j * 128));
         }
       }
     };
@@ -816,10 +848,18 @@ int launch_kv_g(const DecodeLaunch &L, hipStream_t st) {
   if (L.unit_mode) {
     if (L.kv_start) return (int)hipErrorInvalidValue;
     dim3 ugrid((unsigned)L.num_seqs * L.num_kv_heads);
-    if (L.out_dtype == PA_BF16)
-      hipLaunchKernelGGL((decode_unit_kernel<KV, G, true>), ugrid, dim3(unit_waves(KV, G) * 64), 0, st, L);
-    else
-      hipLaunchKernelGGL((decode_unit_kernel<KV, G, false>), ugrid, dim3(unit_waves(KV, G) * 64), 0, st, L);
+    dim3 ublock(unit_waves(KV, G) * 64);
+    if (L.k_new) {
+      if (!L.v_new || !L.new_slots || !L.k_pool_w || !L.v_pool_w) return (int)hipErrorInvalidValue;
+      if (L.out_dtype == PA_BF16)
+        hipLaunchKernelGGL((decode_unit_kernel<KV, G, true, true>), ugrid, ublock, 0, st, L);
+      else
+        hipLaunchKernelGGL((decode_unit_kernel<KV, G, false, true>), ugrid, ublock, 0, st, L);
+    } else if (L.out_dtype == PA_BF16) {
+      hipLaunchKernelGGL((decode_unit_kernel<KV, G, true, false>), ugrid, ublock, 0, st, L);
+    } else {
+      hipLaunchKernelGGL((decode_unit_kernel<KV, G, false, false>), ugrid, ublock, 0, st, L);
+    }
     return (int)hipGetLastError();
   }
   dim3 grid((L.num_workers + NW - 1) / NW);

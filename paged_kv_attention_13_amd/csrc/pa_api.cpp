@@ -56,6 +56,27 @@ pa_status pa_decode(const pa_decode_args *a, void *stream) {
   return pa_merge_partials(a, stream);
 }
 
+pa_status pa_append_decode(const pa_append_args *app, const pa_decode_args *dec, void *stream) {
+  pa_status s = check_append_decode_pair(app, dec, true);
+  if (s != PA_OK || dec->num_seqs == 0) return s;
+  pa_plan plan;
+  DecodeLaunch L;
+  s = prepare_decode(dec, &plan, &L);
+  if (s != PA_OK) return s;
+  if (L.unit_mode) {
+    // one launch: each unit's workgroup appends its row's new token and attends over it
+    L.k_new = app->k;
+    L.v_new = app->v;
+    L.new_slots = app->slot_mapping;
+    L.k_pool_w = app->k_pool;
+    L.v_pool_w = app->v_pool;
+    return hip_status(launch_decode_partials(L, stream), "append + decode");
+  }
+  s = pa_append(app, stream);
+  if (s != PA_OK) return s;
+  return pa_decode(dec, stream);
+}
+
 pa_status pa_append(const pa_append_args *a, void *stream) {
   pa_status s = validate_append(a, true);
   if (s != PA_OK || a->num_tokens == 0) return s;

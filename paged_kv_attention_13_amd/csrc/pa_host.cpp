@@ -523,6 +523,23 @@ pa_status check_rows(const pa_decode_args *a, const int32_t *qsl, int n_dec, int
 
 }  // namespace
 
+pa_status check_append_decode_pair(const pa_append_args *app, const pa_decode_args *dec,
+                                   bool need_device_pointers) {
+  if (!app || !dec) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  pa_status s = validate_append(app, need_device_pointers);
+  if (s != PA_OK) return s;
+  s = validate_decode(dec, need_device_pointers);
+  if (s != PA_OK) return s;
+  if (app->num_tokens != dec->num_seqs)
+    return set_error(PA_ERR_BAD_SHAPE, "num_tokens=%d != num_seqs=%d: one new token per decode row",
+                     app->num_tokens, dec->num_seqs);
+  if (app->k_pool != dec->k_pool || app->v_pool != dec->v_pool || app->kv_dtype != dec->kv_dtype ||
+      app->num_kv_heads != dec->num_kv_heads || app->block_size != dec->block_size ||
+      app->num_blocks != dec->num_blocks || app->k_scale != dec->k_scale || app->v_scale != dec->v_scale)
+    return set_error(PA_ERR_BAD_SHAPE, "the append and decode arguments must describe the same pools");
+  return PA_OK;
+}
+
 }  // namespace pa
 
 using namespace pa;
@@ -586,6 +603,27 @@ pa_status pa_check_append_metadata(const pa_append_args *a) {
       if (used[(size_t)sl]) return set_error(PA_ERR_BAD_METADATA, "slot %d written by two tokens", sl);
       used[(size_t)sl] = 1;
     }
+  }
+  return PA_OK;
+}
+
+pa_status pa_check_append_decode_metadata(const pa_append_args *app, const pa_decode_args *dec) {
+  pa_status s = check_append_decode_pair(app, dec, false);
+  if (s != PA_OK) return s;
+  s = pa_check_append_metadata(app);
+  if (s != PA_OK) return s;
+  s = pa_check_decode_metadata(dec);
+  if (s != PA_OK) return s;
+  // token b is row b's newest position
+  for (int b = 0; b < dec->num_seqs; ++b) {
+    const int32_t slot = app->slot_mapping[b];
+    if (slot < 0) continue;
+    const int pos = dec->seq_lens[b] - 1;
+    const int64_t want = (int64_t)dec->block_table[(size_t)b * dec->max_blocks_per_seq + pos / dec->block_size] *
+                             dec->block_size + pos % dec->block_size;
+    if (slot != want)
+      return set_error(PA_ERR_BAD_METADATA, "slot_mapping[%d]=%d is not the slot of row %d's position %d (%lld)",
+                       b, slot, b, pos, (long long)want);
   }
   return PA_OK;
 }

@@ -73,6 +73,14 @@ struct DecodeLaunch {
   int out_dtype;
   float scale;
   int unit_mode;       // 1: one workgroup per (row, kv head) unit, no workspace, no merge
+  // fused append (unit mode only): row b's new token k_new/v_new[b] ([B][Hkv][D], the pool
+  // dtype) is written to slot new_slots[b] (-1: none) of the pools, and used for position
+  // seq_len - 1 instead of reading that slot
+  const void *k_new;
+  const void *v_new;
+  const int32_t *new_slots;
+  void *k_pool_w;
+  void *v_pool_w;
 };
 
 struct PrefillLaunch {
@@ -185,6 +193,9 @@ pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers);
 pa_status plan_decode(const pa_decode_args *a, pa_plan *plan);
 pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, DecodeLaunch *L);
 pa_status validate_append(const pa_append_args *a, bool need_device_pointers);
+// pa_append_decode: both argument sets valid, one new token per decode row, same pools.
+pa_status check_append_decode_pair(const pa_append_args *app, const pa_decode_args *dec,
+                                   bool need_device_pointers);
 size_t elem_bytes(int dtype);
 // Sub-plans of a pa_mixed call: decode rows, verify rows, prefill rows.  Workspace:
 // decode part first, then the verify part at verify_offset, then the prefill

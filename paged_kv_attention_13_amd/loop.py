@@ -131,10 +131,11 @@ class DecodeLoop:
         return calls
 
     def _launch_decode(self, calls) -> None:
+        # one pa_append_decode per layer: for short rows a single launch appends the new
+        # token and attends over it; otherwise it queues the append and the decode
         s = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
         for a, d, _ in calls:
-            binding.check(binding.LIB.pa_append(ctypes.byref(a), s))
-            binding.check(binding.LIB.pa_decode(ctypes.byref(d), s))
+            binding.check(binding.LIB.pa_append_decode(ctypes.byref(a), ctypes.byref(d), s))
 
     def prepare_decode(self, B: int) -> None:
         self._calls = self._decode_calls(B)

@@ -488,3 +488,48 @@ def test_argument_structs_keep_their_tensors_alive(b):
                            torch.zeros(4, 8, 16, 128), torch.zeros(4, 8, 16, 128))
     gc.collect()
     assert any(t.data_ptr() == a.slot_mapping for t in a._keep)
+
+
+def _pair(b, **kw):
+    """Append args for 4 tokens and decode args for 4 rows over the same pools."""
+    app = _append_args(b)
+    dec = _args(b, num_seqs=4, num_blocks=10, max_blocks_per_seq=8)
+    dec.k_pool = dec.v_pool = app.k_pool
+    for k, v in kw.items():
+        setattr(app, k, v)
+    return app, dec
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_tokens=3), "PA_ERR_BAD_SHAPE"),                 # one new token per decode row
+    (dict(k_pool=0x20000), "PA_ERR_BAD_SHAPE"),               # a different pool
+    (dict(block_size=32), "PA_ERR_BAD_SHAPE"),
+    (dict(num_blocks=11), "PA_ERR_BAD_SHAPE"),
+    (dict(head_dim=64), "PA_ERR_UNSUPPORTED"),                # the append args are validated too
+])
+def test_append_decode_pair_validation(b, kw, status):
+    app, dec = _pair(b, **kw)
+    rc = b.LIB.pa_append_decode(ctypes.byref(app), ctypes.byref(dec), None)
+    assert b.STATUS_NAMES[rc] == status, b.LIB.pa_last_error()
+
+
+def test_append_decode_metadata_checker(b):
+    """Token b must go to the slot of row b's newest position."""
+    import numpy as np
+    bs = 16
+    table = np.array([[3, 1, -1], [0, 2, 4]], dtype=np.int32)
+    lens = np.array([20, 33], dtype=np.int32)
+    slots = np.array([1 * bs + 3, 4 * bs + 0], dtype=np.int32)   # positions 19 and 32
+    app = b.AppendArgs()
+    app.num_tokens, app.num_kv_heads, app.head_dim, app.block_size, app.num_blocks = 2, 8, 128, bs, 5
+    app.src_dtype = app.kv_dtype = b.PA_BF16
+    app.slot_mapping = slots.ctypes.data
+    dec = _args(b, num_seqs=2, num_blocks=5, max_blocks_per_seq=3, max_seq_len=48)
+    dec.block_table, dec.seq_lens = table.ctypes.data, lens.ctypes.data
+    dec.k_pool = dec.v_pool = app.k_pool = app.v_pool = None
+    assert b.LIB.pa_check_append_decode_metadata(ctypes.byref(app), ctypes.byref(dec)) == 0, b.LIB.pa_last_error()
+    slots[1] = 4 * bs + 1                                       # one past row 1's newest position
+    rc = b.LIB.pa_check_append_decode_metadata(ctypes.byref(app), ctypes.byref(dec))
+    assert b.STATUS_NAMES[rc] == "PA_ERR_BAD_METADATA"
+    slots[1] = -1                                               # a skipped token is allowed
+    assert b.LIB.pa_check_append_decode_metadata(ctypes.byref(app), ctypes.byref(dec)) == 0
