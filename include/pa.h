@@ -209,10 +209,14 @@ typedef struct pa_plan {
 int pa_abi_version(void);
 
 /* Validate host-visible arguments and compute the decode plan.  The plan is a
- * pure function of (num_seqs, Hq, Hkv, kv_dtype, max_seq_len, num_workers):
- * it never reads device memory and never synchronises.  The workspace holds,
- * for every (row, kv head) unit, the first worker covering it and their count
- * (2 x int32), then (units + workers) partial slots of Hq/Hkv x (128 + 2) fp32. */
+ * pure function of (num_seqs, Hq, Hkv, kv_dtype, block_size, max_seq_len,
+ * num_workers): it never reads device memory and never synchronises.  With
+ * num_workers == 0, rows bounded by max_seq_len <= 1024 tokens (and 64 pages)
+ * of an fp32 or bf16 cache run one workgroup per (row, kv head) whose waves
+ * combine their results in LDS: workspace_bytes is 0 and num_workers reports
+ * those waves.  Otherwise the workspace holds, for every (row, kv head) unit,
+ * the first worker covering it and their count (2 x int32), then
+ * (units + workers) partial slots of Hq/Hkv x (128 + 2) fp32. */
 pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
 
 /* Workspace bytes a pa_mixed call needs: its decode rows' split-K partials, its
@@ -225,12 +229,14 @@ pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes);
  * log-sum-exp merge kernel, both queued on `stream`.  The decode kernel cuts
  * the flattened (row, kv head, tile) work into num_workers equal contiguous
  * ranges (the split over the context that the dileepadev page names
- * Flash-Decoding, section "Core Optimization Technologies"). */
+ * Flash-Decoding, section "Core Optimization Technologies").  Short rows on the
+ * plan's one-workgroup-per-unit path take a single launch (see pa_decode_plan). */
 pa_status pa_decode(const pa_decode_args *a, void *stream);
 
-/* The two stages of pa_decode, callable separately (e.g. to time one).
- * pa_decode_partials writes `out` for every (row, kv head) unit that one
- * worker covers whole; for a unit cut by worker boundaries it writes, per
+/* The two stages of pa_decode, callable separately (e.g. to time one).  On the
+ * one-workgroup-per-unit plan pa_decode_partials writes every output and
+ * pa_merge_partials does nothing.  Otherwise pa_decode_partials writes `out`
+ * for every (row, kv head) unit that one worker covers whole; for a unit cut by worker boundaries it writes, per
  * piece and query head, the running max m (log2 domain), the sum l of
  * exp2(s - m) and the unnormalised sum of exp2(s - m) V into the workspace,
  * plus the unit's (first worker, count) record.  pa_merge_partials combines
