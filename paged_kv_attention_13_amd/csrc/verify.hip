@@ -579,16 +579,35 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   const int cnt = p.seg_count[u];
   if (cnt <= 1) return;                    // written directly by its only worker
   const int first = p.seg_first[u];
+  // the pieces' maxima, one per lane: one round trip however many pieces there are
   float M = kNegBig;
-  for (int i = 0; i < cnt; ++i) M = fmaxf(M, p.part_m[(size_t)(u + first + i) * p.slot_cols + c]);
+  for (int base = 0; base < cnt; base += 64)
+    if (base + lane < cnt) M = fmaxf(M, p.part_m[(size_t)(u + first + base + lane) * p.slot_cols + c]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  // then the pieces in order, eight at a time with all their loads issued before use
   float n0 = 0.f, n1 = 0.f, den = 0.f;
-  for (int i = 0; i < cnt; ++i) {
-    const size_t slot = (size_t)(u + first + i) * p.slot_cols + c;
-    const float wt = fast_exp2(p.part_m[slot] - M);
-    den = __builtin_fmaf(wt, p.part_l[slot], den);
-    const float2 a = *reinterpret_cast<const float2 *>(p.part_acc + slot * D + 2 * lane);
-    n0 = __builtin_fmaf(wt, a.x, n0);
-    n1 = __builtin_fmaf(wt, a.y, n1);
+  for (int base = 0; base < cnt; base += 8) {
+    float pm[8], pl[8];
+    float2 pa[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (base + k < cnt) {
+        const size_t slot = (size_t)(u + first + base + k) * p.slot_cols + c;
+        pm[k] = p.part_m[slot];
+        pl[k] = p.part_l[slot];
+        pa[k] = *reinterpret_cast<const float2 *>(p.part_acc + slot * D + 2 * lane);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (base + k < cnt) {
+        const float wt = fast_exp2(pm[k] - M);
+        den = __builtin_fmaf(wt, pl[k], den);
+        n0 = __builtin_fmaf(wt, pa[k].x, n0);
+        n1 = __builtin_fmaf(wt, pa[k].y, n1);
+      }
+    }
   }
   const size_t o = ((size_t)(qbase + c / G) * p.num_q_heads + g * G + c % G) * D + 2 * lane;
   if constexpr (OUT_BF16) {
