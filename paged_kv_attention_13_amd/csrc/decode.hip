@@ -12,8 +12,12 @@
 // "Introduction to TensorRT-LLM" (dileepadev.github.io), section "Core
 // Optimization Technologies".
 //
-// Work decomposition.  The work is the flattened sequence of (row, kv head,
-// 16-token tile) units, cut into equal contiguous
+// Work decomposition.  Short rows (bounded by 1,024 tokens, worker count left
+// to the library) run decode_unit_kernel: one workgroup per (row, kv head),
+// its waves merged in LDS, no workspace and no merge launch (and, for
+// pa_append_decode, the row's new token appended in the same launch).
+// Otherwise the work is the flattened sequence of (row, kv head, 16-token
+// tile) units, cut into equal contiguous
 // ranges, one per worker wave; the launch holds about as many waves as the
 // chip keeps resident, so there is no tail of late workgroups and no empty
 // workgroup for short rows.  Each wave streams its range on its own (no LDS,

@@ -13,7 +13,10 @@
 // contractions run on the matrix cores.
 //
 // Tiling.  A workgroup (4 x wave64) owns one (row, kv head, block of query
-// heads, query tile); each wave owns 32 query positions of one query head.
+// heads, query tile) unit -- or, when the launch has at most 256 units, one kv
+// piece of it (the unit's tiles cut into up to 4 pieces whose partials the
+// merge kernel combines); query tiles are dispatched longest first.  Each wave
+// owns 32 query positions of one query head.
 // K/V are staged through two LDS buffers in tiles of 64 tokens gathered page
 // by page through the block table: while tile j is computed, tile j+1 sits in
 // the other buffer and tile j+2's global loads are in flight; one barrier per
