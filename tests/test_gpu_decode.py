@@ -275,3 +275,14 @@ def test_named_workload_full_size(i):
     compare(got[rows], ref[rows], tol, what=f"workload {i} rows {rows[:6]}...")
     # every row (not only the sampled ones) is finite
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("workers", [0, 9])
+def test_one_very_long_row(workers):
+    """One row of 131,072 tokens in 128-token blocks (1,024 pages: 16 block-table chunks of 64,
+    256 MiB per pool) next to a one-token row."""
+    _announce(f"131072-token row, workers={workers}")
+    w = _small([131072, 1], bs=128, seed=80 + workers, extra_blocks=1)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, out_dtype="f32", num_workers=workers)
+    compare(got, ref, 5e-3, what="very long row")

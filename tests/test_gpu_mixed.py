@@ -173,3 +173,13 @@ def test_mixed_graph_replays_match_eager():
         binding.mixed_args_call(me)                      # eager work between the replays
         torch.cuda.synchronize()
         assert torch.equal(out_g, out_e), rep
+
+
+def test_prefill_after_a_100k_prefix():
+    """64 new tokens after 100,000 cached ones in 16-token blocks: each kv piece spans more
+    block-table entries than the kernel stages in LDS, so its loads read the table itself."""
+    _announce("prefill after a 100k prefix")
+    w = _mixed([], [(100000, 64), (3, 5)], seed=91)
+    ref = oracle.paged_attention_workload(w)
+    got = run_mixed(w, out_dtype="f32")
+    compare(got, ref, 1e-2, what="prefill after 100k")
