@@ -450,7 +450,9 @@ def main():
         pl = binding.plan(a)
         ws = torch.empty(max(pl.workspace_bytes, 16), dtype=torch.uint8, device="cuda")
         a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
-        stages = (lambda: binding.decode_partials(a), lambda: binding.merge_partials(a))
+        # rows on the one-workgroup-per-unit path (no workspace) have no merge stage
+        unit_path = pl.workspace_bytes == 0
+        stages = (lambda: binding.decode_partials(a), None if unit_path else (lambda: binding.merge_partials(a)))
         step = None
         n_dec, n_ver = w.num_seqs, 0
 
@@ -468,7 +470,8 @@ def main():
             stages[0]()
             if evs:
                 evs[1].record()
-            stages[1]()
+            if stages[1] is not None:
+                stages[1]()
             if evs:
                 evs[2].record()
 
@@ -504,13 +507,21 @@ def main():
     split_bytes = cb["kv"] + cb["scales"] + cb["q"] + cb["meta"]
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = split_bytes / (kernel_ms * 1e-3) / 1e9
+    if mixed:
+        kernel_label = "pa_mixed call (all kernels)"
+    elif w.kv_fmt == "fp8":
+        kernel_label = "verify_kernel (multi-query kernel on FP8 decode rows, partials)"
+    elif stages[1] is None:
+        kernel_label = "decode_unit_kernel (one workgroup per row and kv head, whole call)"
+    else:
+        kernel_label = "decode_kernel (balanced split, partials)"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if mixed else committed_traffic(w.kv_fmt, w.name),
-                "kernel": "decode_kernel (balanced split, partials)" if not mixed else "pa_mixed call (all kernels)",
+                "kernel": kernel_label,
                 "kernel_ms_mean": round(kernel_ms, 5), "kernel_ms_p10": round(float(np.percentile(k_ms, 10)), 5),
                 "kernel_ms_p90": round(float(np.percentile(k_ms, 90)), 5),
-                "merge_ms_mean": round(float(np.mean(m_ms)), 5),
+                "merge_ms_mean": None if (stages and stages[1] is None) else round(float(np.mean(m_ms)), 5),
                 "bytes_per_launch": int(split_bytes)}
     flops = accounting.call_flops(w.seq_lens, w.q_lens, w.num_q_heads, w.head_dim)
 
