@@ -44,6 +44,10 @@ def parse():
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
     ap.add_argument("--loop-batch", type=int, default=1,
                     help="--op loop: decode rows in the steady batch")
+    ap.add_argument("--scrub-mib", type=int, default=0,
+                    help="decode workloads: write this many MiB between timed steps (outside their events) "
+                         "so no step reads KV left in the caches by the previous one; the step time is then "
+                         "the median of the per-step events")
     ap.add_argument("--prefill-case", default="w5-rows",
                     help="--op prefill: w5-rows, chunk256-after8192 or prompt8192")
     ap.add_argument("--op", default="decode",
@@ -489,13 +493,18 @@ def main():
     torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    scrub = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device="cuda") if args.scrub_mib > 0 else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if scrub is not None:
+            scrub.fill_(i & 255)
         run_step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    if scrub is not None:
+        ms_per_step = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
     k_ms = [e[0].elapsed_time(e[1]) for e in evs]
     m_ms = [e[1].elapsed_time(e[2]) for e in evs]
     kernel_ms = float(np.mean(k_ms))
@@ -545,7 +554,8 @@ def main():
                    "decode_rows": w.num_decode_rows if mixed else w.num_seqs,
                    "verify_rows": n_ver if mixed else 0,
                    "decode_workers": pl.num_workers if pl.num_workers and (not mixed or n_dec) else None,
-                   "tile_tokens": pl.tile_tokens},
+                   "tile_tokens": pl.tile_tokens,
+                   "scrub_mib_between_steps": args.scrub_mib},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_per_step * 1e-3), 1),
