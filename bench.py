@@ -64,6 +64,23 @@ def parse():
     return ap.parse_args()
 
 
+def gpu_state():
+    """Clock and power of the GPU right after the timed region (rocm-smi, read only), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+    except Exception:
+        return None
+    keep = {}
+    for k, v in card.items():
+        kl = k.lower()
+        if "sclk" in kl or "mclk" in kl or "power" in kl:
+            keep[k] = v
+    return keep or None
+
+
 def committed_traffic(kv_fmt: str, workload_name: str):
     """HBM bytes per launch of the decode kernel from the committed counter summary.
 
@@ -569,6 +586,7 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+    res["gpu_state_after_timing"] = gpu_state()
     print(json.dumps(res), flush=True)
 
 
