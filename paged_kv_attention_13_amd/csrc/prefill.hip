@@ -242,8 +242,10 @@ void prefill_kernel(PrefillLaunch p) {
     for (int i = 0; i < CHUNKS; ++i)
       *reinterpret_cast<u32x4 *>(kb + (4 * c_tq + i) * K_STRIDE + c_dg * 16) = rk[i];
     // V^T: for element d = 8*dg + e, the 4 tokens 4*tq .. +3 become one 8-byte group of row d,
-    // stored at group tq ^ (d >> 3) (XOR swizzle: conflict-free stores and loads)
-    const int vgrp = 8 * (c_tq ^ c_dg);
+    // stored at group tq ^ ((d >> 3) & 11): an XOR swizzle that leaves bit 2 of the group alone,
+    // so an operand's low token group always sits 32 bytes below its high one (one paired
+    // read, no register reordering); conflict-free loads, 2-way conflicts on the stores
+    const int vgrp = 8 * (c_tq ^ (c_dg & 11));
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t lo01 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x05040100u);   // e=2w:   t0 t1
@@ -364,13 +366,13 @@ void prefill_kernel(PrefillLaunch p) {
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        // row d = 16 dt + lq of V^T, groups (8 ks2 + 4 half + lg) ^ (d >> 3): the XOR splits
-        // into bits, so the address is a lane base (two variants, by dt's parity) plus an
-        // immediate -- no per-read address arithmetic
+        // row d = 16 dt + lq of V^T, groups (8 ks2 + 4 half + lg) ^ ((d >> 3) & 11): the XOR
+        // splits into bits, so the address is a lane base (two variants, by dt's parity) plus
+        // an immediate -- no per-read address arithmetic -- and the high half is 32 bytes up
         const char *vrow = vb + ((dt & 1) ? vt_lane_odd : vt_lane_even) + 16 * dt * V_STRIDE;
         const int g_hi = 8 * (8 * (ks2 ^ ((dt >> 2) & 1)));
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + g_hi + 8 * 4 * ((dt >> 1) & 1));
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + g_hi + 8 * 4 * (((dt >> 1) & 1) ^ 1));
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + g_hi);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + g_hi + 32);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = mfma(a, pb[qt2][ks2], o[dt][qt2]);
