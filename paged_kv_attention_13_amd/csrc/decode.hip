@@ -17,10 +17,10 @@
 // its waves merged in LDS, no workspace and no merge launch (and, for
 // pa_append_decode, the row's new token appended in the same launch).
 // Otherwise the work is the flattened sequence of (row, kv head, 16-token
-// tile) units, cut into equal contiguous
-// ranges, one per worker wave; the launch holds about as many waves as the
-// chip keeps resident, so there is no tail of late workgroups and no empty
-// workgroup for short rows.  Each wave streams its range on its own (no LDS,
+// tile) units, each unit preceded by a few virtual tiles that stand for its
+// start-up cost, cut into equal contiguous ranges, one per worker wave; the
+// launch holds about as many waves as the chip keeps resident, so there is
+// no tail of late workgroups and no empty workgroup for short rows.  Each wave streams its range on its own (no LDS,
 // no barriers).  A unit covered by one wave is finished and written
 // directly; a unit cut by a range boundary leaves one partial (m, l, acc) per
 // piece, which the merge kernel combines with the log-sum-exp identity --
@@ -146,12 +146,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
     else return p.seq_lens[r];
   };
 
-  // ---- this worker's share of the flattened (row, kv head, tile) space ----
+  // Each unit counts unit_cost extra virtual tiles ahead of its real ones: starting a
+  // unit (query and block-table loads, filling and draining the load pipeline, the
+  // store) costs about that much time, so a worker given many short units gets fewer
+  // tiles.  Virtual tiles are never loaded; a worker whose range holds only a unit's
+  // virtual tiles skips it.
+  const int C = p.unit_cost;
+  auto vtiles = [&](int span) -> int {
+    const int t = (span + TILE - 1) / TILE;
+    return t > 0 ? t + C : 0;
+  };
+
+  // ---- this worker's share of the flattened (row, kv head, virtual tile) space ----
   long long W = 0;
   int n_first = 0, incl_first = 0;         // the first 64 rows' counts, kept for the search below
   for (int base = 0; base < B; base += 64) {
     const int r = base + lane;
-    const int n = r < B ? (span_of(r) + TILE - 1) / TILE : 0;
+    const int n = r < B ? vtiles(span_of(r)) : 0;
     const int incl = wave_inclusive_scan(n, lane);
     if (base == 0) {
       n_first = n;
@@ -179,7 +190,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
     long long before = 0;
     for (int base = 0; base < B; base += 64) {
       const int r = base + lane;
-      const int n = base == 0 ? n_first : (r < B ? (span_of(r) + TILE - 1) / TILE : 0);
+      const int n = base == 0 ? n_first : (r < B ? vtiles(span_of(r)) : 0);
       const int incl = base == 0 ? incl_first : wave_inclusive_scan(n, lane);
       const long long lo = before + (long long)(incl - n) * Hkv;
       const long long hi = before + (long long)incl * Hkv;
@@ -202,17 +213,39 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
 
   int L = span_of(b);
   int nb = (L + TILE - 1) / TILE;
-  int g = (int)((x0 - rowstart) / nb);
-  int t0 = (int)((x0 - rowstart) % nb);
-  long long ustart = rowstart + (long long)g * nb;
+  int vnb = nb + C;
+  int g = (int)((x0 - rowstart) / vnb);
+  int tv = (int)((x0 - rowstart) % vnb);
+  long long ustart = rowstart + (long long)g * vnb;
   long long x = x0;
 
   while (x < x1) {
-    const int cnt = (int)min((long long)(nb - t0), x1 - x);
+    const int cntv = (int)min((long long)(vnb - tv), x1 - x);
+    // the real tiles [t0, t0 + cnt) of this unit in this worker's range
+    const int t0 = max(tv - C, 0);
+    const int cnt = tv + cntv - C - t0;
+    auto next_unit = [&]() {
+      x += cntv;
+      tv = 0;
+      ustart += vnb;
+      if (++g == Hkv) {
+        g = 0;
+        ++b;
+        if (x < x1) {
+          L = span_of(b);
+          nb = (L + TILE - 1) / TILE;
+          vnb = nb + C;
+        }
+      }
+    };
+    if (cnt <= 0) {
+      next_unit();
+      continue;
+    }
     const int u = b * Hkv + g;
     if (t0 == 0 && lane == 0) {
       p.seg_first[u] = worker;
-      p.seg_count[u] = worker_of(ustart + nb - 1) - worker + 1;
+      p.seg_count[u] = worker_of(ustart + C + nb - 1) - worker + 1;
     }
     const bool whole = !CASCADE && t0 == 0 && cnt == nb;
     const int tok_begin = t0 * TILE;
@@ -484,18 +517,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
       }
     }
 
-    // next unit
-    x += cnt;
-    t0 = 0;
-    ustart += nb;
-    if (++g == Hkv) {
-      g = 0;
-      ++b;
-      if (x < x1) {
-        L = span_of(b);
-        nb = (L + TILE - 1) / TILE;
-      }
-    }
+    next_unit();
   }
 }
 

@@ -150,6 +150,7 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   L->num_workers = plan.num_workers;
   L->workers_auto = a->num_workers == 0;
   L->min_tiles = kMinTilesPerWorker;
+  L->unit_cost = kDecodeUnitCost;
   L->kv_dtype = a->kv_dtype;
   L->out_dtype = a->out_dtype;
   L->scale = a->scale;

@@ -27,6 +27,9 @@ constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
 constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
 constexpr int kVerifyMaxWorkers = kTargetCUs * 4;   // one verify wave per SIMD
 constexpr int kMqUnitCost = 4;           // multi-query kernel: start-up cost of a unit, in tiles
+constexpr int kDecodeUnitCost = 4;       // decode kernel: start-up cost of a unit, in 16-token
+                                         // tiles (measured: each unit a wave starts delays its
+                                         // end by ~4.5 us, the time of ~3.6 tiles)
 constexpr int kUnitMaxTokens = 1024;     // decode: rows bounded by this many tokens (and 64
                                          // pages) run one workgroup per (row, kv head) unit
 // waves of that workgroup: 8, or 4 where the per-wave state is large (fp32 pools,
@@ -69,6 +72,7 @@ struct DecodeLaunch {
   int workers_auto;    // 1 when the library chose num_workers (the kernel may use fewer)
   int min_tiles;       // with workers_auto: at least this many tiles per worker (the plan
                        // only knows an upper bound of the row lengths)
+  int unit_cost;       // virtual tiles charged per unit in the work split
   int kv_dtype;
   int out_dtype;
   float scale;
