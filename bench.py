@@ -65,9 +65,20 @@ def parse():
     return ap.parse_args()
 
 
+def under_profiler() -> bool:
+    """True when a rocprofv3 tool library is preloaded into this process."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def gpu_state():
-    """Clock and power of the GPU right after the timed region (rocm-smi, read only), or None."""
+    """Clock and power of the GPU right after the timed region (rocm-smi, read only), or None.
+
+    Skipped under a profiler: its preloaded library would initialise the GPU in the forked
+    child before rocm-smi's interpreter replaces it.
+    """
     import subprocess
+    if under_profiler():
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
                            text=True, timeout=20)
