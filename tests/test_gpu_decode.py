@@ -217,6 +217,22 @@ def test_many_workers_more_than_tiles():
     compare(got, ref, 5e-3, what="surplus workers")
 
 
+@pytest.mark.parametrize("workers", [150, 600, 1500])
+def test_workers_holding_only_start_up_tiles(workers):
+    """Each (row, kv head) unit is charged a few virtual start-up tiles in the work split; with
+    many one-token rows and short ranges, some workers hold only virtual tiles (they skip the
+    unit) and the real tiles of one unit still go to consecutive workers."""
+    _announce(f"virtual start-up tiles, {workers} workers")
+    lens = [1] * 40 + [2000] + [1, 17, 1] * 5
+    w = _small(lens, seed=19)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, out_dtype="f32", num_workers=workers)
+    compare(got, ref, 5e-3, what=f"virtual tiles, {workers} workers")
+    w.v_pool[...] = np.uint16(0x4000)       # 2.0
+    pa_inputs.poison_pool(w)
+    np.testing.assert_array_equal(run_decode(w, out_dtype="f32", num_workers=workers), 2.0)
+
+
 def test_stages_equal_one_call():
     """pa_decode_partials followed by pa_merge_partials equals pa_decode."""
     _announce("stages")
