@@ -154,6 +154,10 @@ void verify_kernel(VerifyLaunch p) {
   constexpr int KR = FP8 ? 4 : 8;          // 16-byte K registers per tile and lane
   constexpr int VR = FP8 ? 4 : 8;          // 16-byte V registers per tile and lane
   __shared__ __attribute__((aligned(16))) char s_vt[NW][VT_BYTES];
+  // FP8 K tile (32 tokens x 128 code bytes) of each wave: loaded as whole 128-byte token
+  // rows, read back in the MFMA operand layout
+  constexpr int KQ_BYTES = FP8 ? TILE * D : 16;
+  __shared__ __attribute__((aligned(16))) char s_kq[NW][KQ_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,6 +178,7 @@ void verify_kernel(VerifyLaunch p) {
   const int tq8 = lane & 7;
   const int dg8 = lane >> 3;
   char *vt = s_vt[wave];
+  char *kq = s_kq[wave];
 
   // tokens each item covers (a group's shared prefix may be empty: no tiles)
   auto len_of = [&](int r) -> int {
@@ -334,10 +339,12 @@ void verify_kernel(VerifyLaunch p) {
         vbase[tb] = vpool + (size_t)phys * phys_stride;
         const uint32_t krow = (uint32_t)(((tok0 + lq) & (bs - 1)) * (D * EB));
         if constexpr (FP8) {
+          // each load instruction covers 8 whole token rows (lane: token lane/8 + 8h, 16
+          // bytes at 16 (lane % 8)); the rows reach the operand layout through LDS
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            k[2 * tb + h] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(kp + krow + 16 * (lg + 4 * h)));
+            k[2 * tb + h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                kp + (uint32_t)(((tok0 + (lane >> 3) + 8 * h) & (bs - 1)) * D) + 16 * (lane & 7)));
         } else {
           const uint32_t voff = (uint32_t)(((tok0 + 4 * tqa) & (bs - 1)) * (D * 2) + 16 * dg);
 #pragma unroll
@@ -359,10 +366,16 @@ void verify_kernel(VerifyLaunch p) {
       }
     };
 
-    // MFMA A operand of k step kk for token half tb (bf16 pairs)
-    auto k_operand = [&](const u32x4 (&k)[KR], int tb, int kk) -> u32x4 {
+    // FP8 K rows in this wave's LDS tile: token t's 16-byte group g sits at group
+    // g ^ ((t >> 1) & 7) of its 128-byte row, so 16 consecutive lanes of a write (tokens t,
+    // t + 1, all 8 groups) or of a read (16 tokens, one group) touch 16 different 16-byte
+    // bank groups of a 256-byte bank row
+    auto kq_addr = [&](int t, int g) -> int { return t * D + 16 * (g ^ ((t >> 1) & 7)); };
+    // MFMA A operand of k step kk for token half tb (bf16 pairs); FP8: kc[tb][kk / 2] holds
+    // 16 code bytes of token 16 tb + lq, elements 16 (lg + 4 (kk / 2)) .. +16
+    auto k_operand = [&](const u32x4 (&k)[KR], const u32x4 (&kc)[2][2], int tb, int kk) -> u32x4 {
       if constexpr (FP8) {
-        const u32x4 c = k[2 * tb + (kk >> 1)];
+        const u32x4 c = kc[tb][kk >> 1];
         const uint32_t w0 = (kk & 1) ? c[2] : c[0];
         const uint32_t w1 = (kk & 1) ? c[3] : c[1];
         return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
@@ -415,6 +428,20 @@ void verify_kernel(VerifyLaunch p) {
           *reinterpret_cast<u32x4 *>(vt + vt_offset(8 * dg + e, tqa)) = grp;
         }
       }
+      u32x4 kc[2][2];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<u32x4 *>(kq + kq_addr(16 * tb + (lane >> 3) + 8 * h, lane & 7)) = k[2 * tb + h];
+        wave_lds_fence();
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            kc[tb][h] = *reinterpret_cast<const u32x4 *>(kq + kq_addr(16 * tb + lq, lg + 4 * h));
+      }
       // ---- S^T = K Q^T ----
       f32x4 s[2][NCB];
 #pragma unroll
@@ -425,7 +452,7 @@ void verify_kernel(VerifyLaunch p) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const u32x4 a = k_operand(k, tb, kk);
+          const u32x4 a = k_operand(k, kc, tb, kk);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) s[tb][cb] = mfma(a, qb[cb][kk], s[tb][cb]);
         }
