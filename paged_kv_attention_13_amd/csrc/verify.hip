@@ -117,6 +117,18 @@ __device__ __forceinline__ int vt_offset(int d, int gi) {
   return blk * 256 + (4 * quarter + (gi ^ (blk & 3))) * 16;
 }
 
+// V^T layout of FP8 pools, whose transposing writes are 8 bytes wide (4 tokens of one row d):
+// row d's 64 bytes sit in quarter ((d & 3) + d / 16) mod 4 of 256-byte block d / 4, its
+// 16-byte groups XOR-ed with (d / 4 + d / 16) mod 4.  Under a 64-bank model each half-wave of
+// writes (rows 16 dg + 4 w + e for four dg, all groups and halves) and each 16-lane operand
+// read (rows 16 db + 0..15, one group) touch distinct banks (the bf16 layout above leaves the
+// 8-byte writes two-way conflicted).
+__device__ __forceinline__ int vt_offset8(int d, int gi) {
+  const int r = d >> 4;
+  const int quarter = ((d & 3) + r) & 3;
+  return (d >> 2) * 256 + 64 * quarter + 16 * (gi ^ (((d >> 2) + r) & 3));
+}
+
 // Keeps the compiler from moving this wave's LDS accesses across the point;
 // the LDS itself serves one wave's accesses in issue order.
 __device__ __forceinline__ void wave_lds_fence() {
@@ -407,13 +419,13 @@ void verify_kernel(VerifyLaunch p) {
           const uint32_t y01 = __builtin_amdgcn_perm(v[1][w], v[0][w], 0x07030602u);   // t0b2 t1b2 t0b3 t1b3
           const uint32_t y23 = __builtin_amdgcn_perm(v[3][w], v[2][w], 0x07030602u);
           const int d = 16 * dg8 + 4 * w;
-          *reinterpret_cast<u32x2 *>(vt + vt_offset(d, tq8 & 3) + half) =
+          *reinterpret_cast<u32x2 *>(vt + vt_offset8(d, tq8 & 3) + half) =
               u32x2{fp8x2_to_bf16x2<false>(x01), fp8x2_to_bf16x2<false>(x23)};
-          *reinterpret_cast<u32x2 *>(vt + vt_offset(d + 1, tq8 & 3) + half) =
+          *reinterpret_cast<u32x2 *>(vt + vt_offset8(d + 1, tq8 & 3) + half) =
               u32x2{fp8x2_to_bf16x2<true>(x01), fp8x2_to_bf16x2<true>(x23)};
-          *reinterpret_cast<u32x2 *>(vt + vt_offset(d + 2, tq8 & 3) + half) =
+          *reinterpret_cast<u32x2 *>(vt + vt_offset8(d + 2, tq8 & 3) + half) =
               u32x2{fp8x2_to_bf16x2<false>(y01), fp8x2_to_bf16x2<false>(y23)};
-          *reinterpret_cast<u32x2 *>(vt + vt_offset(d + 3, tq8 & 3) + half) =
+          *reinterpret_cast<u32x2 *>(vt + vt_offset8(d + 3, tq8 & 3) + half) =
               u32x2{fp8x2_to_bf16x2<true>(y01), fp8x2_to_bf16x2<true>(y23)};
         }
       } else {
@@ -508,7 +520,8 @@ void verify_kernel(VerifyLaunch p) {
       wave_lds_fence();
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(vt + vt_offset(16 * db + lq, lg));
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(
+            vt + (FP8 ? vt_offset8(16 * db + lq, lg) : vt_offset(16 * db + lq, lg)));
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) o[db][cb] = mfma(a, pb[cb], o[db][cb]);
       }
