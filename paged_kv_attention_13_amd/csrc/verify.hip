@@ -36,10 +36,13 @@
 // FP8-E4M3 pools: codes are widened to bf16 in registers with
 // v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value is a bf16 value), the
 // per-head K scale folded into the softmax scale and the V scale applied to
-// the result.  A lane loads 16 code bytes = 16 consecutive head-dim elements of
-// one token, which feed two MFMA k steps, so K is read with 16-byte loads; the
-// head-dim order of the contraction is permuted to match (and Q^T is read in
-// the same order), which leaves the dot products unchanged.
+// the result.  16 code bytes = 16 consecutive head-dim elements of one token
+// feed two MFMA k steps; the head-dim order of the contraction is permuted to
+// match (and Q^T is read in the same order), which leaves the dot products
+// unchanged.  K is loaded as whole 128-byte token rows (8 rows per load
+// instruction; in the operand layout an instruction would cover half of 16
+// rows) and reaches the operand layout through a wave-private 4 KB LDS tile.
+// FP8 V^T has an LDS layout of its own, conflict-free for its 8-byte writes.
 // Three register sets keep two tiles' loads in flight while one is computed;
 // one wave per SIMD (up to 512 registers).  Tokens at or past the row's end
 // are excluded by select and their V zeroed before the transpose, so NaN in
