@@ -277,10 +277,10 @@ def decode_args_call(args: DecodeArgs, stream=None) -> None:
 def make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *,
                     num_decode_rows: int, max_q_len: int, max_seq_len: int, out=None,
                     num_workers: int = 0, num_verify_rows: int = 0,
-                    max_verify_q_len: int = 0) -> MixedArgs:
+                    max_verify_q_len: int = 0, k_scale=None, v_scale=None) -> MixedArgs:
     m = MixedArgs()
     base = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
-                            out=out, num_workers=num_workers)
+                            k_scale=k_scale, v_scale=v_scale, out=out, num_workers=num_workers)
     m.base = base
     m.q_start_loc = _ptr(q_start_loc)
     m.total_q = int(q.shape[0])
@@ -299,7 +299,8 @@ def mixed_workspace_bytes(m: MixedArgs) -> int:
 
 def mixed(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *, num_decode_rows: int,
           max_q_len: int, max_seq_len: int, out=None, out_dtype=None, num_workers: int = 0,
-          num_verify_rows: int = 0, max_verify_q_len: int = 0, workspace=None, stream=None):
+          num_verify_rows: int = 0, max_verify_q_len: int = 0, k_scale=None, v_scale=None,
+          workspace=None, stream=None):
     """Mixed batch (``pa_mixed``): decode rows, then verify rows, then prefill-chunk rows.
     Returns ``out`` [total_q, Hq, D]."""
     if out is None:
@@ -307,7 +308,8 @@ def mixed(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *, num_d
     m = make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale,
                         num_decode_rows=num_decode_rows, max_q_len=max_q_len,
                         max_seq_len=max_seq_len, out=out, num_workers=num_workers,
-                        num_verify_rows=num_verify_rows, max_verify_q_len=max_verify_q_len)
+                        num_verify_rows=num_verify_rows, max_verify_q_len=max_verify_q_len,
+                        k_scale=k_scale, v_scale=v_scale)
     if workspace is None:
         workspace = _alloc_workspace(mixed_workspace_bytes(m), q.device)
     if workspace is not None:

@@ -34,7 +34,8 @@ def run_mixed(w, out_dtype=None, num_workers=0, dev=None, num_verify_rows=0):
                         d["q_start_loc"], w.scale, num_decode_rows=nd,
                         max_q_len=int(prefill_q.max()) if len(prefill_q) else 1,
                         max_seq_len=w.max_seq_len, out_dtype=odt, num_workers=num_workers,
-                        num_verify_rows=nv, max_verify_q_len=int(verify_q.max()) if nv else 0)
+                        num_verify_rows=nv, max_verify_q_len=int(verify_q.max()) if nv else 0,
+                        k_scale=d["k_scale"], v_scale=d["v_scale"])
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64)
 

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import pa_inputs
-from gpu_util import TOL_BF16, compare, run_decode, run_mixed
+from gpu_util import TOL_BF16, TOL_FP8, compare, run_decode, run_mixed
 
 pytestmark = pytest.mark.gpu
 
@@ -17,13 +17,13 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def _verify(rows, dec_lens=(), pre=(), bs=16, hq=32, hkv=8, seed=0, poison=True):
+def _verify(rows, dec_lens=(), pre=(), bs=16, hq=32, hkv=8, seed=0, poison=True, kv_fmt="bf16"):
     """rows: (L, n) verify rows; dec_lens: decode rows placed first; pre: (prior, n) prefill rows last."""
     L = list(dec_lens) + [l for l, _ in rows] + [p + n for p, n in pre]
     ql = [1] * len(dec_lens) + [n for _, n in rows] + [n for _, n in pre]
     w = pa_inputs.make_workload(name="verify", seq_lens=L, q_lens=ql, num_q_heads=hq, num_kv_heads=hkv,
                                 head_dim=128, block_size=bs, seed=seed, extra_blocks=3,
-                                poison_unused=poison)
+                                poison_unused=poison, kv_fmt=kv_fmt)
     w.num_decode_rows = len(dec_lens)
     return w
 
@@ -39,6 +39,17 @@ def test_verify_ragged(bs, workers):
     ref = oracle.paged_attention_workload(w)
     got = run_mixed(w, num_workers=workers, num_verify_rows=len(ROWS))
     compare(got, ref, TOL_BF16, what=f"verify bs{bs} W{workers}")
+
+
+@pytest.mark.parametrize("bs,workers", [(16, 0), (64, 0), (16, 7), (32, 300)])
+def test_verify_fp8_kv(bs, workers):
+    """FP8-E4M3 pools: decode rows and verify rows of up to 8 new tokens in one call, against the
+    oracle fed the dequantised values (NaN codes poison every unused slot)."""
+    _announce(f"verify fp8 bs={bs} workers={workers}")
+    w = _verify(ROWS, dec_lens=[1, 77, 3000], bs=bs, seed=40 + bs + workers, kv_fmt="fp8")
+    ref = oracle.paged_attention_workload(w)
+    got = run_mixed(w, num_workers=workers, num_verify_rows=len(ROWS))
+    compare(got, ref, TOL_FP8, what=f"verify fp8 bs{bs} W{workers}")
 
 
 def test_verify_f32_out():
