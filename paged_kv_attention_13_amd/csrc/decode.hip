@@ -20,10 +20,11 @@
 // tile) units, each unit preceded by a few virtual tiles that stand for its
 // start-up cost, cut into equal contiguous ranges, one per worker wave; the
 // launch holds about as many waves as the chip keeps resident, so there is
-// no tail of late workgroups and no empty workgroup for short rows.  Each wave streams its range on its own (no LDS,
-// no barriers).  A unit covered by one wave is finished and written
-// directly; a unit cut by a range boundary leaves one partial (m, l, acc) per
-// piece, which the merge kernel combines with the log-sum-exp identity --
+// no tail of late workgroups and no empty workgroup for short rows.  Each
+// wave streams its range on its own (no LDS, no barriers).  A unit covered by
+// one wave is finished and written directly; a unit cut by a range boundary
+// leaves one partial (m, l, acc) per piece, which the merge kernel combines
+// with the log-sum-exp identity --
 // the split over the context named Flash-Decoding on the dileepadev page.
 // Inside a wave, 8 lanes share one token: each lane holds 16 of its 128
 // elements, loaded with 16-byte loads so that one load instruction covers
