@@ -233,6 +233,18 @@ def test_workers_holding_only_start_up_tiles(workers):
     np.testing.assert_array_equal(run_decode(w, out_dtype="f32", num_workers=workers), 2.0)
 
 
+@pytest.mark.parametrize("workers", [0, 37, 1500])
+def test_many_short_rows(workers):
+    """700 rows of 1..300 tokens: the split's prefix scan and row search run over 11 chunks of 64
+    rows (workers 37 and 1,500), or every (row, kv head) gets its own workgroup (workers 0)."""
+    _announce(f"700 short rows, {workers} workers")
+    lens = np.random.default_rng(23).integers(1, 301, size=700)
+    w = _small(lens.tolist(), seed=23)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, out_dtype="f32", num_workers=workers)
+    compare(got, ref, 5e-3, what=f"700 rows, {workers} workers")
+
+
 def test_stages_equal_one_call():
     """pa_decode_partials followed by pa_merge_partials equals pa_decode."""
     _announce("stages")
