@@ -101,18 +101,17 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
   const int tile = tile_tokens(a->kv_dtype);
   int nw = a->num_workers;
   if (nw == 0) {
-    // about as many waves as the chip keeps resident, but at least a few tiles each
+    // one wave per SIMD at most (whole workgroups, one per CU: on every shape measured, from
+    // a single row of 8,192 tokens to 55 rows of 8,192, equal to or up to 26 % faster than two
+    // waves per SIMD), but at least a few tiles each.  FP8 pools run on the multi-query
+    // kernel (one column per query head), with its own resident-wave count.
     const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
     const int64_t tiles_upper = units * ((a->max_seq_len + tile - 1) / tile);
-    nw = (int)std::min<int64_t>(kMaxWorkers, std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) /
-                                                                     kMinTilesPerWorker));
-    // FP8 pools run on the multi-query kernel (one column per query head)
-    if (a->kv_dtype == PA_FP8_E4M3)
-      nw = std::min(nw, mq_max_workers(a->kv_dtype, a->num_q_heads / a->num_kv_heads));
-    // enough work: one wave per SIMD (whole workgroups, one per CU) streams HBM better than
-    // two (measured from 32 to 512 tiles per wave: equal or 2-10 % faster)
-    else if (nw == kMaxWorkers && tiles_upper >= (int64_t)kLongRowTiles * (kMaxWorkers / 2))
-      nw = kMaxWorkers / 2;
+    const int cap = a->kv_dtype == PA_FP8_E4M3
+                        ? mq_max_workers(a->kv_dtype, a->num_q_heads / a->num_kv_heads)
+                        : kDecodeMaxWorkers;
+    nw = (int)std::min<int64_t>(cap, std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) /
+                                                              kMinTilesPerWorker));
   }
   plan->num_workers = nw;
   plan->tile_tokens = tile;

@@ -14,12 +14,8 @@ namespace pa {
 constexpr int kHeadDim = 128;
 constexpr int kWavesPerBlock = 4;        // decode kernel: 4 independent wave64 workers per workgroup
 constexpr int kTargetCUs = 256;          // MI355X compute units (grid planning only)
-constexpr int kWorkersPerCU = 8;         // resident decode waves per CU (2 per SIMD)
-constexpr int kMaxWorkers = kTargetCUs * kWorkersPerCU;
+constexpr int kDecodeMaxWorkers = kTargetCUs * 4;   // decode kernel: one wave per SIMD
 constexpr int kMinTilesPerWorker = 4;    // below this, fewer workers are launched
-constexpr int kLongRowTiles = 32;        // decode: from this many tiles per wave at one wave per
-                                         // SIMD (as bounded by max_seq_len), the plan launches
-                                         // one wave per SIMD
 constexpr int kCascadeRowMinTiles = 12;  // shared-prefix calls, row parts: every piece is a
                                          // partial, so pieces are kept longer
 constexpr int kCascadePrefixMinTiles = 2;   // shared-prefix calls, prefix part: few, long units;

@@ -113,7 +113,7 @@ def test_null_struct(b):
 
 
 def test_plan_choices(b):
-    # enough work (>= 32 tiles per wave at one wave per SIMD): one worker per SIMD
+    # one worker per SIMD at most
     a = _args(b, num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192)
     p = b.plan(a)
     assert p.num_workers == 1024 and p.tile_tokens == 16
@@ -126,11 +126,13 @@ def test_plan_choices(b):
     a.kv_dtype = 2
     a.k_scale = a.v_scale = 0x10000
     assert b.plan(a).tile_tokens == 32
-    # 32 rows of up to 4,096 tokens: 64 tiles per wave at one wave per SIMD
+    a = _args(b, num_seqs=8, block_size=16, max_blocks_per_seq=128, max_seq_len=2048)
+    assert b.plan(a).num_workers == 1024
     a = _args(b, num_seqs=32, block_size=16, max_blocks_per_seq=256, max_seq_len=4096)
     assert b.plan(a).num_workers == 1024
-    # less work: two waves per SIMD, as many as the chip keeps resident
-    a = _args(b, num_seqs=8, block_size=16, max_blocks_per_seq=128, max_seq_len=2048)
+    # FP8 pools: the multi-query kernel, up to two waves per SIMD
+    a.kv_dtype = 2
+    a.k_scale = a.v_scale = 0x10000
     assert b.plan(a).num_workers == 2048
     # an explicit worker count is honoured
     a = _args(b, num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192, num_workers=7)
