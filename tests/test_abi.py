@@ -141,6 +141,11 @@ def test_plan_choices(b):
     a = _args(b, num_seqs=1, max_seq_len=2048, max_blocks_per_seq=128)
     p = b.plan(a)
     assert p.num_workers == 8 * 128 // 4
+    # rows within 1,024 tokens and at most 512 (row, kv head) units: one workgroup per unit
+    a = _args(b, num_seqs=64, max_seq_len=300, max_blocks_per_seq=64)
+    assert b.plan(a).workspace_bytes == 0
+    a = _args(b, num_seqs=65, max_seq_len=300, max_blocks_per_seq=64)
+    assert b.plan(a).workspace_bytes > 0 and b.plan(a).num_workers == 1024
     # rows within 1,024 tokens: one workgroup of 8 waves per (row, kv head), no workspace
     a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
     p = b.plan(a)

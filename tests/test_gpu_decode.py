@@ -233,16 +233,23 @@ def test_workers_holding_only_start_up_tiles(workers):
     np.testing.assert_array_equal(run_decode(w, out_dtype="f32", num_workers=workers), 2.0)
 
 
-@pytest.mark.parametrize("workers", [0, 37, 1500])
-def test_many_short_rows(workers):
-    """700 rows of 1..300 tokens: the split's prefix scan and row search run over 11 chunks of 64
-    rows (workers 37 and 1,500), or every (row, kv head) gets its own workgroup (workers 0)."""
-    _announce(f"700 short rows, {workers} workers")
-    lens = np.random.default_rng(23).integers(1, 301, size=700)
+@pytest.mark.parametrize("rows,workers", [(700, 0), (700, 37), (700, 1500), (64, 0), (65, 0)])
+def test_many_short_rows(rows, workers):
+    """Rows of 1..300 tokens.  700 rows: the split's prefix scan and row search run over 11 chunks
+    of 64 rows.  With the worker count left to the library, 64 rows (512 units) still run one
+    workgroup per (row, kv head) and 65 rows (520 units) go to the balanced split."""
+    _announce(f"{rows} short rows, {workers} workers")
+    from paged_kv_attention_13_amd import binding
+    from paged_kv_attention_13_amd.device import to_device
+    lens = np.random.default_rng(23).integers(1, 301, size=rows)
     w = _small(lens.tolist(), seed=23)
+    d = to_device(w)
+    a = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], w.scale,
+                                 max_seq_len=w.max_seq_len, num_workers=workers)
+    assert (binding.plan(a).workspace_bytes == 0) == (workers == 0 and rows * 8 <= 512)
     ref = oracle.paged_attention_workload(w)
-    got = run_decode(w, out_dtype="f32", num_workers=workers)
-    compare(got, ref, 5e-3, what=f"700 rows, {workers} workers")
+    got = run_decode(w, out_dtype="f32", num_workers=workers, dev=d)
+    compare(got, ref, 5e-3, what=f"{rows} rows, {workers} workers")
 
 
 def test_stages_equal_one_call():
