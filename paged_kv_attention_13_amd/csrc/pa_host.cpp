@@ -101,17 +101,25 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
   const int tile = tile_tokens(a->kv_dtype);
   int nw = a->num_workers;
   if (nw == 0) {
-    // one wave per SIMD at most (whole workgroups, one per CU: on every shape measured, from
-    // a single row of 8,192 tokens to 55 rows of 8,192, equal to or up to 26 % faster than two
-    // waves per SIMD), but at least a few tiles each.  FP8 pools run on the multi-query
+    // One wave per SIMD (whole workgroups, one per CU) when units can be long: measured equal
+    // to or 2-26 % faster than two waves per SIMD from units of 64 to 2,048 tiles (a single
+    // 32,768-token row: 40.5 vs 55 us).  Two waves per SIMD when every unit is short (at most
+    // 32 tiles): 3-9 % faster (2,048 rows of 128 tokens: 233 vs 251 us), the start-ups of more
+    // units overlapping.  At least a few tiles per worker.  FP8 pools run on the multi-query
     // kernel (one column per query head), with its own resident-wave count.
     const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
-    const int64_t tiles_upper = units * ((a->max_seq_len + tile - 1) / tile);
-    const int cap = a->kv_dtype == PA_FP8_E4M3
-                        ? mq_max_workers(a->kv_dtype, a->num_q_heads / a->num_kv_heads)
-                        : kDecodeMaxWorkers;
+    const int64_t unit_tiles = (a->max_seq_len + tile - 1) / tile;
+    const bool fp8 = a->kv_dtype == PA_FP8_E4M3;
+    // the decode kernel's split also counts each unit's virtual start-up tiles
+    const int64_t tiles_upper = units * (unit_tiles + (fp8 ? 0 : kDecodeUnitCost));
+    const bool short_units = !fp8 && unit_tiles <= kShortUnitTiles;
+    const int cap = fp8 ? mq_max_workers(a->kv_dtype, a->num_q_heads / a->num_kv_heads)
+                        : (short_units ? 2 * kDecodeMaxWorkers : kDecodeMaxWorkers);
     nw = (int)std::min<int64_t>(cap, std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) /
                                                               kMinTilesPerWorker));
+    // a second wave on only some SIMDs leaves the others idle at the end: whole rounds only
+    // (600 rows of 16 tokens: 1,200 workers 52.6 us, 1,024 46.3 us, 2,048 40.6 us)
+    if (short_units && nw > kDecodeMaxWorkers) nw = 2 * kDecodeMaxWorkers;
   }
   plan->num_workers = nw;
   plan->tile_tokens = tile;

@@ -14,7 +14,10 @@ namespace pa {
 constexpr int kHeadDim = 128;
 constexpr int kWavesPerBlock = 4;        // decode kernel: 4 independent wave64 workers per workgroup
 constexpr int kTargetCUs = 256;          // MI355X compute units (grid planning only)
-constexpr int kDecodeMaxWorkers = kTargetCUs * 4;   // decode kernel: one wave per SIMD
+constexpr int kDecodeMaxWorkers = kTargetCUs * 4;   // decode kernel: one wave per SIMD ...
+constexpr int kShortUnitTiles = 32;      // ... or two when no unit (row, kv head) exceeds this
+                                         // many tiles: short units are bound by their start-up
+                                         // latency, which more resident waves overlap
 constexpr int kMinTilesPerWorker = 4;    // below this, fewer workers are launched
 constexpr int kCascadeRowMinTiles = 12;  // shared-prefix calls, row parts: every piece is a
                                          // partial, so pieces are kept longer

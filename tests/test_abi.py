@@ -140,12 +140,21 @@ def test_plan_choices(b):
     # tiny work with an explicit split: fewer workers, at least a few tiles each
     a = _args(b, num_seqs=1, max_seq_len=2048, max_blocks_per_seq=128)
     p = b.plan(a)
-    assert p.num_workers == 8 * 128 // 4
+    assert p.num_workers == 8 * (128 + 4) // 4       # each unit's 4 virtual start-up tiles count
     # rows within 1,024 tokens and at most 512 (row, kv head) units: one workgroup per unit
     a = _args(b, num_seqs=64, max_seq_len=300, max_blocks_per_seq=64)
     assert b.plan(a).workspace_bytes == 0
     a = _args(b, num_seqs=65, max_seq_len=300, max_blocks_per_seq=64)
-    assert b.plan(a).workspace_bytes > 0 and b.plan(a).num_workers == 1024
+    assert b.plan(a).workspace_bytes > 0
+    # many short units (at most 32 tiles each): two waves per SIMD
+    assert b.plan(a).num_workers == 2048
+    a = _args(b, num_seqs=2048, max_seq_len=128, max_blocks_per_seq=8)
+    assert b.plan(a).num_workers == 2048
+    a = _args(b, num_seqs=2048, max_seq_len=513, max_blocks_per_seq=33)
+    assert b.plan(a).num_workers == 1024
+    # short units between one and two waves per SIMD round up to two
+    a = _args(b, num_seqs=130, max_seq_len=64, max_blocks_per_seq=4)   # 1,040 units x 8 tiles
+    assert b.plan(a).num_workers == 2048
     # rows within 1,024 tokens: one workgroup of 8 waves per (row, kv head), no workspace
     a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
     p = b.plan(a)
