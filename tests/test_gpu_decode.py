@@ -73,6 +73,16 @@ def test_fp8_ragged(workers):
     compare(got, ref, TOL_FP8, what=f"fp8 W{workers}")
 
 
+@pytest.mark.parametrize("hq,hkv,bs", [(8, 8, 16), (16, 8, 32), (64, 8, 16), (12, 3, 64), (4, 1, 128)])
+def test_fp8_group_sizes(hq, hkv, bs):
+    """FP8 pools for every group size (1, 2, 4, 8 query heads per kv head) and block size."""
+    _announce(f"fp8 group hq={hq} hkv={hkv} bs={bs}")
+    w = _small(RAGGED, kv_fmt="fp8", hq=hq, hkv=hkv, bs=bs, seed=hq + hkv + bs)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, out_dtype="f32")
+    compare(got, ref, TOL_FP8, what=f"fp8 G={hq // hkv} bs{bs}")
+
+
 def test_fp8_every_code_decodes_exactly():
     """Single cached token: out = v_scale * E4M3(code), every one of the 256 codes."""
     _announce("fp8 all codes")
