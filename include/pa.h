@@ -212,9 +212,13 @@ int pa_abi_version(void);
  * pure function of (num_seqs, Hq, Hkv, kv_dtype, block_size, max_seq_len,
  * num_workers): it never reads device memory and never synchronises.  With
  * num_workers == 0, rows bounded by max_seq_len <= 1024 tokens (and 64 pages)
- * of an fp32 or bf16 cache run one workgroup per (row, kv head) whose waves
- * combine their results in LDS: workspace_bytes is 0 and num_workers reports
- * those waves.  Otherwise the workspace holds, for every (row, kv head) unit,
+ * of an fp32 or bf16 cache, at most 512 (row, kv head) units, run one
+ * workgroup per unit whose waves combine their results in LDS: workspace_bytes
+ * is 0 and num_workers reports those waves.  Otherwise, with num_workers == 0
+ * the plan takes one worker wave per SIMD (1,024), or two (2,048) when no unit
+ * can exceed 32 tiles or the cache is FP8, fewer for small work (at least 4
+ * tiles each, counting 4 start-up tiles per unit for fp32/bf16 caches); the
+ * workspace holds, for every (row, kv head) unit,
  * the first worker covering it and their count (2 x int32), then
  * (units + workers) partial slots of Hq/Hkv x (128 + 2) fp32. */
 pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
@@ -276,8 +280,8 @@ pa_status pa_check_append_metadata(const pa_append_args *a_host);
  * describe the same pools, and slot_mapping[b] is -1 or the slot of position
  * seq_lens[b] - 1 of row b (pa_check_append_decode_metadata verifies this on
  * host copies).  When the decode plan runs one workgroup per (row, kv head)
- * (rows within 1,024 tokens, worker count left to the library, fp32 or bf16
- * pools) this is one launch: each workgroup writes its row's new K/V to the
+ * (rows within 1,024 tokens, at most 512 units, worker count left to the
+ * library, fp32 or bf16 pools) this is one launch: each workgroup writes its row's new K/V to the
  * slot and takes position seq_len - 1 from the new rows rather than from the
  * slot, so no part of the launch reads memory it writes.  Otherwise the two
  * calls are queued one after the other.  For a decode loop whose layers each
