@@ -64,6 +64,17 @@ def test_fp32_path():
     compare(got, ref, TOL_F32, rel_tol=1e-5, what="fp32")
 
 
+@pytest.mark.parametrize("hq,hkv,workers", [(8, 8, 0), (16, 8, 77), (64, 8, 0), (64, 8, 300), (12, 3, 5)])
+def test_fp32_group_sizes(hq, hkv, workers):
+    """fp32 pools for every group size, through the one-workgroup-per-unit kernel (rows within
+    1,024 tokens, workers 0) and the balanced split."""
+    _announce(f"fp32 group hq={hq} hkv={hkv} workers={workers}")
+    w = _small(RAGGED, q_fmt="f32", kv_fmt="f32", hq=hq, hkv=hkv, seed=90 + hq + workers)
+    ref = oracle.paged_attention_workload(w)
+    got = run_decode(w, num_workers=workers)
+    compare(got, ref, TOL_F32, rel_tol=1e-5, what=f"fp32 G={hq // hkv} W{workers}")
+
+
 @pytest.mark.parametrize("workers", [0, 3, 111])
 def test_fp8_ragged(workers):
     _announce(f"fp8 ragged workers={workers}")
