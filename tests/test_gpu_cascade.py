@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import pa_inputs
-from gpu_util import TOL_BF16, compare, run_cascade, run_decode
+from gpu_util import TOL_BF16, TOL_REL_L2, compare, run_cascade, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -137,7 +137,8 @@ def test_cascade_full_size_workload():
     _announce(f"workload 7: {pa_inputs.WORKLOAD_NAMES[7]}")
     w = pa_inputs.make_config(7)
     got = run_cascade(w)
-    assert np.all(np.isfinite(got))
-    rows = [0, 9, 31, 63]
-    ref = oracle.paged_attention_workload(w, rows=rows)
-    compare(got[rows], ref[rows], TOL_BF16, what=f"workload 7 rows {rows}")
+    ref = oracle.paged_attention_workload(w)
+    compare(got, ref, TOL_BF16, what=f"workload 7, all {w.num_seqs} rows")
+    for b in range(w.num_seqs):
+        rel = np.linalg.norm(got[b] - ref[b]) / np.linalg.norm(ref[b])
+        assert rel <= TOL_REL_L2, (b, rel)

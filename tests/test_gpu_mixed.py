@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import pa_inputs
-from gpu_util import TOL_BF16, compare, run_mixed
+from gpu_util import TOL_BF16, TOL_REL_L2, compare, run_mixed
 
 pytestmark = pytest.mark.gpu
 
@@ -123,12 +123,12 @@ def test_mixed_full_size_workload():
     _announce(f"workload 5: {pa_inputs.WORKLOAD_NAMES[5]}")
     w = pa_inputs.make_config(5)
     got = run_mixed(w)
-    assert np.all(np.isfinite(got))
-    rng = np.random.default_rng(5)
-    rows = sorted(set(rng.choice(96, size=6, replace=False).tolist()) | {96, 99, 103})
-    ref = oracle.paged_attention_workload(w, rows=rows)
-    idx = np.concatenate([np.arange(w.q_start_loc[b], w.q_start_loc[b + 1]) for b in rows])
-    compare(got[idx], ref[idx], TOL_BF16, what=f"workload 5 rows {rows}")
+    ref = oracle.paged_attention_workload(w)
+    compare(got, ref, TOL_BF16, what=f"workload 5, all {w.num_seqs} rows ({w.total_q} queries)")
+    for b in range(w.num_seqs):
+        a, e = w.q_start_loc[b], w.q_start_loc[b + 1]
+        rel = np.linalg.norm(got[a:e] - ref[a:e]) / np.linalg.norm(ref[a:e])
+        assert rel <= TOL_REL_L2, (b, rel)
 
 
 def test_mixed_graph_replays_match_eager():

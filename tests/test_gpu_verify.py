@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import pa_inputs
-from gpu_util import TOL_BF16, TOL_FP8, compare, run_decode, run_mixed
+from gpu_util import TOL_BF16, TOL_FP8, TOL_REL_L2, compare, run_decode, run_mixed
 
 pytestmark = pytest.mark.gpu
 
@@ -177,8 +177,9 @@ def test_verify_full_size_workload():
     _announce(f"workload 6: {pa_inputs.WORKLOAD_NAMES[6]}")
     w = pa_inputs.make_config(6)
     got = run_mixed(w, num_verify_rows=w.num_seqs)
-    assert np.all(np.isfinite(got))
-    rows = [0, 17, 54]
-    ref = oracle.paged_attention_workload(w, rows=rows)
-    idx = np.concatenate([np.arange(w.q_start_loc[b], w.q_start_loc[b + 1]) for b in rows])
-    compare(got[idx], ref[idx], TOL_BF16, what=f"workload 6 rows {rows}")
+    ref = oracle.paged_attention_workload(w)
+    compare(got, ref, TOL_BF16, what=f"workload 6, all {w.num_seqs} rows ({w.total_q} queries)")
+    for b in range(w.num_seqs):
+        a, e = w.q_start_loc[b], w.q_start_loc[b + 1]
+        rel = np.linalg.norm(got[a:e] - ref[a:e]) / np.linalg.norm(ref[a:e])
+        assert rel <= TOL_REL_L2, (b, rel)
