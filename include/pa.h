@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 /* Element types.  Supported (q, kv, out) combinations:
  *   (F32, F32, F32|BF16), (BF16, BF16, BF16|F32), (BF16, FP8_E4M3, BF16|F32). */
@@ -120,7 +120,8 @@ typedef struct pa_decode_args {
   const float *v_scale;        /* [Hkv], same rule */
   const int32_t *block_table;  /* [B][max_blocks_per_seq] */
   const int32_t *seq_lens;     /* [B], tokens in cache including the new one, >= 1 */
-  float scale;                 /* softmax scale (1/sqrt(D) for standard attention) */
+  float scale;                 /* softmax scale (1/sqrt(D) for standard attention); launching
+                                  calls require it finite and > 0 (PA_ERR_UNSUPPORTED otherwise) */
   void *out;                   /* [B][Hq][D], out_dtype */
   void *workspace;             /* split records and partials (pa_decode_plan); NULL only when B == 0 */
   size_t workspace_bytes;
@@ -210,18 +211,28 @@ int pa_abi_version(void);
 
 /* Validate host-visible arguments and compute the decode plan.  The plan is a
  * pure function of (num_seqs, Hq, Hkv, kv_dtype, block_size, max_seq_len,
- * num_workers): it never reads device memory and never synchronises.  With
- * num_workers == 0, rows bounded by max_seq_len <= 1024 tokens (and 64 pages)
- * of an fp32 or bf16 cache, at most 512 (row, kv head) units, run one
+ * num_workers) and of the current device's compute-unit count C (read once per
+ * device; 256 on MI355X): it never reads device memory and never synchronises.
+ * With num_workers == 0, rows bounded by max_seq_len <= 1024 tokens (and 64
+ * pages) of an fp32 or bf16 cache, at most 2C (row, kv head) units, run one
  * workgroup per unit whose waves combine their results in LDS: workspace_bytes
  * is 0 and num_workers reports those waves.  Otherwise, with num_workers == 0
- * the plan takes one worker wave per SIMD (1,024), or two (2,048) when no unit
- * can exceed 32 tiles or the cache is FP8, fewer for small work (at least 4
- * tiles each, counting 4 start-up tiles per unit for fp32/bf16 caches); the
+ * the plan takes one worker wave per SIMD (4C), or two (8C) when no unit can
+ * exceed 32 tiles or the cache is FP8, fewer for small work (at least 4 tiles
+ * each, counting 4 start-up tiles per unit for fp32/bf16 caches); the
  * workspace holds, for every (row, kv head) unit,
  * the first worker covering it and their count (2 x int32), then
  * (units + workers) partial slots of Hq/Hkv x (128 + 2) fp32. */
 pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
+
+/* Workspace bytes a pa_decode call with these arguments needs (the plan's
+ * workspace_bytes; 0 on the one-workgroup-per-unit path and for an empty batch).
+ * The caller allocates it (the library allocates nothing) and passes it in
+ * a->workspace.  Returns SIZE_MAX, with pa_last_error() set, when the host-visible
+ * arguments are invalid (the same checks as pa_decode_plan).  The workspace holds
+ * the split-over-the-context partials the dileepadev page names Flash-Decoding
+ * ("Introduction to TensorRT-LLM", section "Core Optimization Technologies"). */
+size_t pa_decode_workspace_size(const pa_decode_args *a);
 
 /* Workspace bytes a pa_mixed call needs: its decode rows' split-K partials, its
  * verify rows' partials and, when the prefill rows make at most 256 (row, kv
@@ -294,6 +305,19 @@ pa_status pa_check_append_decode_metadata(const pa_append_args *app_host, const 
  * q/pool/out pointers are not read. */
 pa_status pa_check_decode_metadata(const pa_decode_args *a_host);
 pa_status pa_check_mixed_metadata(const pa_mixed_args *a_host);
+
+/* Synchronous CPU validator of a whole in-flight batch (decode rows first, then
+ * verify rows, then chunked-prefill rows: "TensorRT-LLM, in depth"
+ * (aicassindra.com), section "In-flight batching and the scheduler"), on HOST
+ * copies of block_table, seq_lens and q_start_loc: every row's block ids in
+ * [0, num_blocks) for its ceil(L / bs) blocks (the ordered per-request block
+ * list of "How does TensorRT-LLM work", section "The paged KV cache"),
+ * 1 <= q_len <= L <= max_seq_len, decode rows of one token at their own q
+ * index, verify and prefill rows within their q_len bounds, and q_start_loc
+ * running from 0 to total_q.  Returns PA_ERR_BAD_METADATA with the first
+ * violation in pa_last_error().  The same check as pa_check_mixed_metadata;
+ * pa_check_decode_metadata is its decode-only form. */
+pa_status pa_check_metadata(const pa_mixed_args *a_host);
 
 const char *pa_status_string(pa_status s);
 const char *pa_last_error(void);

@@ -1,0 +1,41 @@
+/*
+ * pa_probe.h -- measurement probe of the paged-KV attention library: the
+ * achievable HBM streaming-read bandwidth of the device.
+ *
+ * A decode step reads the request's whole KV cache and is bound by memory
+ * bandwidth ("TensorRT-LLM, in depth" (aicassindra.com), section "First
+ * principles: where the GPU memory goes"), so the context number for a decode
+ * kernel's bandwidth is what a plain stream of the same loads reaches on the
+ * same bytes.  This call reads a buffer once with the load form the decode
+ * kernels use (16-byte non-temporal vector loads, whole 64-byte lines per
+ * four lanes) and no other work, so its rate is the ceiling those loads can
+ * reach; the published peak of the HBM stays the roofline.
+ */
+#ifndef PA_PROBE_H_
+#define PA_PROBE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` bytes at `src` (a DEVICE pointer, 16-byte aligned; bytes a
+ * multiple of 16) once, in num_workgroups workgroups of 256 lanes
+ * (1 .. 65536) that walk it in a grid-strided loop with four loads in flight
+ * per lane.  Each wave writes the XOR of the words it read to
+ * out[4 * workgroup + wave] (a DEVICE array of 4 * num_workgroups uint32,
+ * caller-owned), so the loads are not removed; the values mean nothing else.
+ * Queued on `stream`; allocates nothing.  Errors: PA_ERR_NULL_POINTER,
+ * PA_ERR_MISALIGNED, PA_ERR_BAD_SHAPE before any launch; PA_ERR_HIP if the
+ * launch fails. */
+pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t num_workgroups, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_PROBE_H_ */

@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpa_kv.so")
+# PA_LIB_PATH selects another build of the same ABI (the tests load the host-only
+# sanitizer build this way); by default the in-tree HIP library.
+LIB_PATH = os.environ.get("PA_LIB_PATH") or os.path.join(PKG, "libpa_kv.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_ERR_NULL_POINTER", 2: "PA_ERR_BAD_SHAPE", 3: "PA_ERR_BAD_DTYPE",
@@ -24,7 +26,8 @@ EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_d
             "pa_decode_partials", "pa_merge_partials", "pa_mixed", "pa_append", "pa_check_decode_metadata",
             "pa_check_mixed_metadata", "pa_check_append_metadata", "pa_cascade_workspace_size",
             "pa_decode_cascade", "pa_check_cascade_metadata", "pa_append_decode",
-            "pa_check_append_decode_metadata", "pa_status_string", "pa_last_error"]
+            "pa_check_append_decode_metadata", "pa_status_string", "pa_last_error",
+            "pa_decode_workspace_size", "pa_check_metadata", "pa_stream_read"]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -115,6 +118,10 @@ def _load():
     sigs = {
         "pa_abi_version": ([], ctypes.c_int),
         "pa_decode_plan": ([P(DecodeArgs), P(Plan)], ctypes.c_int),
+        "pa_decode_workspace_size": ([P(DecodeArgs)], ctypes.c_size_t),
+        "pa_check_metadata": ([P(MixedArgs)], ctypes.c_int),
+        "pa_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
+                           ctypes.c_int),
         "pa_mixed_workspace_size": ([P(MixedArgs), P(ctypes.c_size_t)], ctypes.c_int),
         "pa_decode": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_decode_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
@@ -181,6 +188,24 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+class _on_stream:
+    """Make ``stream`` (if given) torch's current stream for the duration of a call, so that the
+    output and workspace the call allocates belong to the stream its kernels run on: the caching
+    allocator then does not hand that memory to other streams' work while the kernels use it."""
+
+    def __init__(self, stream):
+        self.ctx = None if stream is None else _torch().cuda.stream(stream)
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            return self.ctx.__exit__(*exc)
+        return False
+
+
 def _hold(struct, *objs):
     """Keep the tensors whose addresses a struct carries alive as long as the struct.
 
@@ -233,6 +258,17 @@ def plan(args: DecodeArgs) -> Plan:
     return p
 
 
+SIZE_MAX = ctypes.c_size_t(-1).value
+
+
+def decode_workspace_bytes(args: DecodeArgs) -> int:
+    """``pa_decode_workspace_size``: bytes of workspace a decode call needs."""
+    n = int(LIB.pa_decode_workspace_size(ctypes.byref(args)))
+    if n == SIZE_MAX:
+        raise PagedAttentionError(2, LIB.pa_last_error().decode())
+    return n
+
+
 def _alloc_out(q, out_dtype):
     torch = _torch()
     return torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
@@ -249,16 +285,17 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq_len: int,
            k_scale=None, v_scale=None, out=None, out_dtype=None, num_workers: int = 0,
            workspace=None, stream=None):
     """Decode attention (``pa_decode``).  Returns ``out`` [B, Hq, D]."""
-    if out is None:
-        out = _alloc_out(q, out_dtype)
-    a = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
-                         k_scale=k_scale, v_scale=v_scale, out=out, num_workers=num_workers)
-    if workspace is None:
-        workspace = _alloc_workspace(plan(a).workspace_bytes, q.device)
-    if workspace is not None:
-        a.workspace = _ptr(workspace)
-        a.workspace_bytes = workspace.numel() * workspace.element_size()
-    check(LIB.pa_decode(ctypes.byref(a), ctypes.c_void_p(_stream(stream))))
+    with _on_stream(stream):
+        if out is None:
+            out = _alloc_out(q, out_dtype)
+        a = make_decode_args(q, k_pool, v_pool, block_table, seq_lens, scale, max_seq_len=max_seq_len,
+                             k_scale=k_scale, v_scale=v_scale, out=out, num_workers=num_workers)
+        if workspace is None:
+            workspace = _alloc_workspace(decode_workspace_bytes(a), q.device)
+        if workspace is not None:
+            a.workspace = _ptr(workspace)
+            a.workspace_bytes = workspace.numel() * workspace.element_size()
+        check(LIB.pa_decode(ctypes.byref(a), ctypes.c_void_p(_stream(stream))))
     return out
 
 
@@ -303,19 +340,20 @@ def mixed(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale, *, num_d
           workspace=None, stream=None):
     """Mixed batch (``pa_mixed``): decode rows, then verify rows, then prefill-chunk rows.
     Returns ``out`` [total_q, Hq, D]."""
-    if out is None:
-        out = _alloc_out(q, out_dtype)
-    m = make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale,
-                        num_decode_rows=num_decode_rows, max_q_len=max_q_len,
-                        max_seq_len=max_seq_len, out=out, num_workers=num_workers,
-                        num_verify_rows=num_verify_rows, max_verify_q_len=max_verify_q_len,
-                        k_scale=k_scale, v_scale=v_scale)
-    if workspace is None:
-        workspace = _alloc_workspace(mixed_workspace_bytes(m), q.device)
-    if workspace is not None:
-        m.base.workspace = _ptr(workspace)
-        m.base.workspace_bytes = workspace.numel() * workspace.element_size()
-    check(LIB.pa_mixed(ctypes.byref(m), ctypes.c_void_p(_stream(stream))))
+    with _on_stream(stream):
+        if out is None:
+            out = _alloc_out(q, out_dtype)
+        m = make_mixed_args(q, k_pool, v_pool, block_table, seq_lens, q_start_loc, scale,
+                            num_decode_rows=num_decode_rows, max_q_len=max_q_len,
+                            max_seq_len=max_seq_len, out=out, num_workers=num_workers,
+                            num_verify_rows=num_verify_rows, max_verify_q_len=max_verify_q_len,
+                            k_scale=k_scale, v_scale=v_scale)
+        if workspace is None:
+            workspace = _alloc_workspace(mixed_workspace_bytes(m), q.device)
+        if workspace is not None:
+            m.base.workspace = _ptr(workspace)
+            m.base.workspace_bytes = workspace.numel() * workspace.element_size()
+        check(LIB.pa_mixed(ctypes.byref(m), ctypes.c_void_p(_stream(stream))))
     return out
 
 
@@ -362,7 +400,7 @@ def check_mixed_metadata(block_table, seq_lens, q_start_loc, *, num_decode_rows:
     m.max_q_len = max_q_len
     m.num_verify_rows = num_verify_rows
     m.max_verify_q_len = max_verify_q_len
-    check(LIB.pa_check_mixed_metadata(ctypes.byref(m)))
+    check(LIB.pa_check_metadata(ctypes.byref(m)))
 
 
 def make_cascade_args(q, k_pool, v_pool, block_table, seq_lens, group_start, shared_len, scale, *,
@@ -388,17 +426,18 @@ def decode_cascade(q, k_pool, v_pool, block_table, seq_lens, group_start, shared
                    max_seq_len: int, max_group_rows: int, out=None, out_dtype=None, num_workers: int = 0,
                    workspace=None, stream=None):
     """Shared-prefix decode (``pa_decode_cascade``).  Returns ``out`` [B, Hq, D]."""
-    if out is None:
-        out = _alloc_out(q, out_dtype)
-    c = make_cascade_args(q, k_pool, v_pool, block_table, seq_lens, group_start, shared_len, scale,
-                          max_seq_len=max_seq_len, max_group_rows=max_group_rows, out=out,
-                          num_workers=num_workers)
-    if workspace is None:
-        workspace = _alloc_workspace(cascade_workspace_bytes(c), q.device)
-    if workspace is not None:
-        c.base.workspace = _ptr(workspace)
-        c.base.workspace_bytes = workspace.numel() * workspace.element_size()
-    check(LIB.pa_decode_cascade(ctypes.byref(c), ctypes.c_void_p(_stream(stream))))
+    with _on_stream(stream):
+        if out is None:
+            out = _alloc_out(q, out_dtype)
+        c = make_cascade_args(q, k_pool, v_pool, block_table, seq_lens, group_start, shared_len, scale,
+                              max_seq_len=max_seq_len, max_group_rows=max_group_rows, out=out,
+                              num_workers=num_workers)
+        if workspace is None:
+            workspace = _alloc_workspace(cascade_workspace_bytes(c), q.device)
+        if workspace is not None:
+            c.base.workspace = _ptr(workspace)
+            c.base.workspace_bytes = workspace.numel() * workspace.element_size()
+        check(LIB.pa_decode_cascade(ctypes.byref(c), ctypes.c_void_p(_stream(stream))))
     return out
 
 
@@ -469,3 +508,10 @@ def check_append_metadata(slot_mapping, *, num_kv_heads: int, head_dim: int, blo
     a.block_size, a.num_blocks, a.src_dtype, a.kv_dtype = block_size, num_blocks, src_dtype, kv_dtype
     a.slot_mapping = sm.ctypes.data
     check(LIB.pa_check_append_metadata(ctypes.byref(a)))
+
+
+def stream_read(src, out, num_workgroups: int, stream=None) -> None:
+    """``pa_stream_read``: read every byte of the device tensor ``src`` once (the bandwidth
+    probe); ``out`` is a device uint32/int32 tensor of 4 * num_workgroups words."""
+    nbytes = src.numel() * src.element_size()
+    check(LIB.pa_stream_read(_ptr(src), nbytes, _ptr(out), int(num_workgroups), ctypes.c_void_p(_stream(stream))))

@@ -53,5 +53,27 @@ def build(verbose: bool = False) -> str:
     return out
 
 
+HOST_SOURCES = ("pa_host.cpp", "pa_api.cpp", "pa_runtime.cpp", os.path.join("host_only", "launch_stubs.cpp"))
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+
+
+def build_host_only(out_dir: str = None, sanitize: bool = True) -> str:
+    """The library's host code (argument checks, plans, metadata checkers, block manager,
+    scheduler) built with g++ as a shared library of the same ABI, every kernel launch
+    replaced by a "no device" error; with ``sanitize``, under AddressSanitizer and
+    UndefinedBehaviorSanitizer.  Returns the path of the built library."""
+    out_dir = out_dir or os.path.join(ROOT, "_build")
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libpa_host_san.so" if sanitize else "libpa_host.so")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-Wall", "-Wno-unused-function",
+           *(SANITIZE if sanitize else []), "-I", INCLUDE, "-I", CSRC,
+           *[os.path.join(CSRC, f) for f in HOST_SOURCES], "-o", out + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed ({r.returncode}):\n{r.stdout}{r.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -37,9 +37,11 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(CascadeMergeLaunch p)
   const int g = h / G;
   const int hh = h % G;
   // the row's own part
+  // piece records are clamped to the slots of the launches' workers, so a record that does
+  // not come from this call's partials gives wrong numbers, never a read outside the workspace
   const int us = b * Hkv + g;
-  const int fs = p.seg_first[us];
-  const int cs = p.seg_count[us];
+  const int fs = min(max(p.seg_first[us], 0), p.row_workers - 1);
+  const int cs = min(max(p.seg_count[us], 0), p.row_workers - fs);
   // its group (last k with group_start[k] <= b) and its column in the group's prefix pieces
   int lo = 0, hi = p.num_groups;
   while (hi - lo > 1) {
@@ -48,10 +50,10 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(CascadeMergeLaunch p)
     else hi = mid;
   }
   const int up = lo * Hkv + g;
-  const int col = (b - p.group_start[lo]) * G + hh;
+  const int col = min(max((b - p.group_start[lo]) * G + hh, 0), p.slot_cols - 1);
   const bool has_prefix = p.shared_len[b] > 0;
-  const int fp = has_prefix ? p.pseg_first[up] : 0;
-  const int cp = has_prefix ? p.pseg_count[up] : 0;
+  const int fp = has_prefix ? min(max(p.pseg_first[up], 0), p.prefix_workers - 1) : 0;
+  const int cp = has_prefix ? min(max(p.pseg_count[up], 0), p.prefix_workers - fp) : 0;
 
   // pieces 0 .. cs-1 are the row's own, cs .. cs+cp-1 the prefix's; lane i holds piece
   // i's (m, l) so that every piece's scalars load at once, then the 128-element

@@ -1,6 +1,7 @@
 // ABI entry points that queue work: validate on the host, then hand the
 // resolved launch description to the kernel launchers.  Plain C++.
 #include "pa_internal.h"
+#include "pa_probe.h"
 
 using namespace pa;
 
@@ -163,6 +164,7 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.scale = b.scale;
     P.splits = mp.prefill_splits;
     P.max_qtiles = mp.prefill_qtiles;
+    P.resident_slots = prefill_slots(mp.cus);
     if (mp.prefill_splits > 1) {
       char *ws = static_cast<char *>(b.workspace);
       P.part_o = reinterpret_cast<float *>(ws + mp.prefill_offset);
@@ -190,6 +192,17 @@ pa_status pa_decode_cascade(const pa_cascade_args *a, void *stream) {
   s = hip_status(launch_decode_partials(d, stream), "decode");
   if (s != PA_OK) return s;
   return hip_status(launch_cascade_merge(m, stream), "cascade merge");
+}
+
+pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t num_workgroups, void *stream) {
+  if (!src || !out) return set_error(PA_ERR_NULL_POINTER, "src and out are required");
+  if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+    return set_error(PA_ERR_MISALIGNED, "src must be 16-byte aligned and out 4-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0)
+    return set_error(PA_ERR_BAD_SHAPE, "bytes=%zu must be a positive multiple of 16", bytes);
+  if (num_workgroups < 1 || num_workgroups > 65536)
+    return set_error(PA_ERR_BAD_SHAPE, "num_workgroups=%d outside [1, 65536]", num_workgroups);
+  return hip_status(launch_stream_read(src, bytes, out, num_workgroups, stream), "stream read");
 }
 
 }  // extern "C"

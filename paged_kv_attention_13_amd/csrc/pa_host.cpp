@@ -91,14 +91,24 @@ pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers) {
       return set_error(PA_ERR_MISALIGNED, "q, k_pool, v_pool and out must be 16-byte aligned");
     if (a->workspace && !aligned16(a->workspace))
       return set_error(PA_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    // the kernels take the running maximum over unscaled scores (prefill) or fold the
+    // scale into exp2 arguments: both need a positive, finite scale
+    if (!(a->scale > 0.0f) || !std::isfinite(a->scale))
+      return set_error(PA_ERR_UNSUPPORTED, "scale=%g must be finite and > 0", (double)a->scale);
   }
   return PA_OK;
 }
 
 int tile_tokens(int kv_dtype) { return kv_dtype == PA_FP8_E4M3 ? 32 : 16; }
 
+// Weak default for builds without the HIP runtime (the host-only test build); the
+// library's device_info.hip provides the real query.
+__attribute__((weak)) int device_cus() { return kDefaultCUs; }
+
 pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
   const int tile = tile_tokens(a->kv_dtype);
+  const int cus = device_cus();
+  const int max_workers = decode_max_workers(cus);
   int nw = a->num_workers;
   if (nw == 0) {
     // One wave per SIMD (whole workgroups, one per CU) when units can be long: measured equal
@@ -113,17 +123,17 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
     // the decode kernel's split also counts each unit's virtual start-up tiles
     const int64_t tiles_upper = units * (unit_tiles + (fp8 ? 0 : kDecodeUnitCost));
     const bool short_units = !fp8 && unit_tiles <= kShortUnitTiles;
-    const int cap = fp8 ? mq_max_workers(a->kv_dtype, a->num_q_heads / a->num_kv_heads)
-                        : (short_units ? 2 * kDecodeMaxWorkers : kDecodeMaxWorkers);
+    const int cap = fp8 ? mq_max_workers(a->kv_dtype, a->num_q_heads / a->num_kv_heads, cus)
+                        : (short_units ? 2 * max_workers : max_workers);
     nw = (int)std::min<int64_t>(cap, std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) /
                                                               kMinTilesPerWorker));
     // a second wave on only some SIMDs leaves the others idle at the end: whole rounds only
     // (600 rows of 16 tokens: 1,200 workers 52.6 us, 1,024 46.3 us, 2,048 40.6 us)
-    if (short_units && nw > kDecodeMaxWorkers) nw = 2 * kDecodeMaxWorkers;
+    if (short_units && nw > max_workers) nw = 2 * max_workers;
   }
   plan->num_workers = nw;
   plan->tile_tokens = tile;
-  if (decode_unit_mode(a)) {
+  if (decode_unit_mode(a, cus)) {
     // one workgroup of 8 (or 4) waves per (row, kv head) unit, merged in LDS
     const int waves = unit_waves(a->kv_dtype, a->num_q_heads / a->num_kv_heads);
     plan->num_workers = (int32_t)std::min<int64_t>((int64_t)a->num_seqs * a->num_kv_heads * waves, INT32_MAX);
@@ -161,7 +171,7 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   L->kv_dtype = a->kv_dtype;
   L->out_dtype = a->out_dtype;
   L->scale = a->scale;
-  L->unit_mode = decode_unit_mode(a);
+  L->unit_mode = decode_unit_mode(a, device_cus());
   if (a->num_seqs > 0 && !L->unit_mode) {
     if (!a->workspace || a->workspace_bytes < plan.workspace_bytes)
       return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, plan needs %zu",
@@ -216,6 +226,8 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPla
     if (b.kv_dtype != PA_BF16)
       return set_error(PA_ERR_UNSUPPORTED, "prefill-chunk rows need a bf16 KV cache and bf16 q");
   }
+  const int cus = device_cus();
+  mp->cus = cus;
   pa_decode_args *dec = &mp->dec;
   pa_plan *dec_plan = &mp->dec_plan;
   int *verify_workers = &mp->verify_workers;
@@ -231,7 +243,7 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPla
     int nw = b.num_workers;
     if (nw == 0) {
       const int64_t tiles_upper = units * ((b.max_seq_len + kVerifyTile - 1) / kVerifyTile);
-      nw = (int)std::min<int64_t>(mq_max_workers(b.kv_dtype, a->max_verify_q_len * G),
+      nw = (int)std::min<int64_t>(mq_max_workers(b.kv_dtype, a->max_verify_q_len * G, cus),
                                   std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) / kMinTilesPerWorker));
     }
     *verify_workers = nw;
@@ -258,8 +270,9 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPla
     const int64_t units_upper = (int64_t)n_pre * b.num_kv_heads * (G / hb) * mp->prefill_qtiles;
     const int64_t tiles_upper = (b.max_seq_len + kPrefillTile - 1) / kPrefillTile;
     int splits = 1;
-    if (units_upper <= kPrefillSlots / 2) {
-      splits = (int)std::min<int64_t>(kPrefillMaxSplits, (2 * kPrefillSlots + units_upper - 1) / units_upper);
+    const int slots = prefill_slots(cus);
+    if (units_upper <= slots / 2) {
+      splits = (int)std::min<int64_t>(kPrefillMaxSplits, (2 * slots + units_upper - 1) / units_upper);
       splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, tiles_upper / kPrefillMinChunkTiles));
     }
     mp->prefill_splits = splits;
@@ -341,7 +354,7 @@ pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, Deco
   if (rows.num_workers == 0) {
     pa_plan p0;
     plan_decode(&rows, &p0);
-    rows.num_workers = std::min(p0.num_workers, kVerifyMaxWorkers);
+    rows.num_workers = std::min(p0.num_workers, verify_max_workers(device_cus()));
   }
   pa_plan dplan;
   plan_decode(&rows, &dplan);
@@ -354,7 +367,7 @@ pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, Deco
     pw = b.num_workers;
     if (pw == 0) {
       const int64_t tiles_upper = (int64_t)punits * ((b.max_seq_len + kVerifyTile - 1) / kVerifyTile);
-      pw = (int)std::min<int64_t>(kVerifyMaxWorkers,
+      pw = (int)std::min<int64_t>(verify_max_workers(device_cus()),
                                   std::max<int64_t>(1, (tiles_upper + kMinTilesPerWorker - 1) / kMinTilesPerWorker));
     }
     const size_t slots = (punits + pw) * (size_t)slot_cols;
@@ -425,6 +438,8 @@ pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, Deco
   mrg->num_kv_heads = b.num_kv_heads;
   mrg->slot_cols = slot_cols;
   mrg->out_dtype = b.out_dtype;
+  mrg->row_workers = dec->num_workers;
+  mrg->prefix_workers = pw;
   return PA_OK;
 }
 
@@ -580,6 +595,12 @@ pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan) {
   return plan_decode(a, plan);
 }
 
+size_t pa_decode_workspace_size(const pa_decode_args *a) {
+  pa_plan plan;
+  if (pa_decode_plan(a, &plan) != PA_OK) return SIZE_MAX;
+  return plan.workspace_bytes;
+}
+
 pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes) {
   if (!a || !bytes) return set_error(PA_ERR_NULL_POINTER, "argument is NULL");
   MixedPlan mp;
@@ -654,6 +675,8 @@ pa_status pa_check_mixed_metadata(const pa_mixed_args *a) {
   return check_rows(&a->base, a->q_start_loc, a->num_decode_rows, a->num_verify_rows, a->max_verify_q_len,
                     a->max_q_len);
 }
+
+pa_status pa_check_metadata(const pa_mixed_args *a) { return pa_check_mixed_metadata(a); }
 
 pa_status pa_cascade_workspace_size(const pa_cascade_args *a, size_t *bytes) {
   if (!a || !bytes) return set_error(PA_ERR_NULL_POINTER, "argument is NULL");

@@ -13,8 +13,12 @@ namespace pa {
 // Shapes the kernels are compiled for.
 constexpr int kHeadDim = 128;
 constexpr int kWavesPerBlock = 4;        // decode kernel: 4 independent wave64 workers per workgroup
-constexpr int kTargetCUs = 256;          // MI355X compute units (grid planning only)
-constexpr int kDecodeMaxWorkers = kTargetCUs * 4;   // decode kernel: one wave per SIMD ...
+constexpr int kDefaultCUs = 256;         // MI355X compute units: the plan's count where no
+                                         // device can be asked (a host-only build)
+// Compute units of the current device, read once per device (device_info.hip).
+int device_cus();
+// decode kernel: one wave per SIMD (4 per CU) ...
+inline int decode_max_workers(int cus) { return cus * 4; }
 constexpr int kShortUnitTiles = 32;      // ... or two when no unit (row, kv head) exceeds this
                                          // many tiles: short units are bound by their start-up
                                          // latency, which more resident waves overlap
@@ -25,21 +29,21 @@ constexpr int kCascadePrefixMinTiles = 2;   // shared-prefix calls, prefix part:
                                             // more workers hide their start-up latency
 constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
 constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
-constexpr int kVerifyMaxWorkers = kTargetCUs * 4;   // one verify wave per SIMD
+inline int verify_max_workers(int cus) { return cus * 4; }   // one verify wave per SIMD
 constexpr int kMqUnitCost = 4;           // multi-query kernel: start-up cost of a unit, in tiles
 constexpr int kDecodeUnitCost = 4;       // decode kernel: start-up cost of a unit, in 16-token
                                          // tiles (measured: each unit a wave starts delays its
                                          // end by ~4.5 us, the time of ~3.6 tiles)
 constexpr int kUnitMaxTokens = 1024;     // decode: rows bounded by this many tokens (and 64
                                          // pages) run one workgroup per (row, kv head) unit
-constexpr int kUnitMaxUnits = 512;       // ... when there are at most this many units (two
-                                         // workgroups per CU); beyond it the balanced split
-                                         // measured 16-29 % faster
+// ... when there are at most two units per CU (512 on 256 CUs); beyond it the balanced
+// split measured 16-29 % faster
+inline int unit_max_units(int cus) { return cus * 2; }
 // waves of that workgroup: 8, or 4 where the per-wave state is large (fp32 pools,
 // or 8 query heads per kv head), which then fits one wave per SIMD without spills
 constexpr int unit_waves(int kv_dtype, int group) { return (kv_dtype == PA_F32 || group >= 8) ? 4 : 8; }
 constexpr int kPrefillTile = 64;         // prefill kernel: kv tokens per tile
-constexpr int kPrefillSlots = kTargetCUs * 2;   // prefill workgroups resident at once (2 per CU)
+inline int prefill_slots(int cus) { return cus * 2; }   // prefill workgroups resident at once (2 per CU)
 constexpr int kPrefillMaxSplits = 4;     // prefill: at most this many kv pieces per unit
 constexpr int kPrefillMinChunkTiles = 4; // prefill: a piece covers at least this many tiles
 constexpr int kPrefillWaves = 4;         // prefill: waves per workgroup, 32 query positions each
@@ -112,6 +116,7 @@ struct PrefillLaunch {
   // pieces of a cut unit go to per-(unit, piece) slots and a merge kernel combines them
   int splits;                    // 1 = no split
   int max_qtiles;                // ceil(max_q_len / QB)
+  int resident_slots;            // prefill workgroups resident at once on the device
   float *part_o;                 // [slot][4 waves][32 q][128] fp32, unnormalised
   float *part_ml;                // [slot][4 waves][32 q][2] fp32: running max (log2 domain), sum
 };
@@ -177,6 +182,8 @@ struct CascadeMergeLaunch {
   int num_kv_heads;
   int slot_cols;
   int out_dtype;
+  int row_workers;               // workers of the row-part launch (its slots: units + workers)
+  int prefix_workers;            // workers of the prefix launch
 };
 
 struct AppendLaunch {
@@ -218,6 +225,7 @@ struct MixedPlan {
   size_t prefill_ml_offset = 0;   // piece (max, sum) pairs
   size_t prefill_slots = 0;
   size_t total_bytes = 0;
+  int cus = kDefaultCUs;          // compute units the plan was made for
 };
 // Checks the pa_mixed row classes and fills the plan.
 pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPlan *mp);
@@ -229,15 +237,15 @@ pa_status make_decode_mq_launch(const pa_decode_args *a, const pa_plan &plan, Ve
 inline bool decode_on_mq(const pa_decode_args *a) { return a->kv_dtype == PA_FP8_E4M3; }
 // Short rows with the worker count left to the library: one workgroup per unit
 // (every row within the first 64 block-table entries and kUnitMaxTokens tokens, at most
-// kUnitMaxUnits units).
-inline bool decode_unit_mode(const pa_decode_args *a) {
+// two units per CU).
+inline bool decode_unit_mode(const pa_decode_args *a, int cus) {
   return a->num_workers == 0 && a->num_seqs > 0 && a->kv_dtype != PA_FP8_E4M3 &&
          a->max_seq_len <= kUnitMaxTokens && a->max_seq_len <= 64 * a->block_size &&
-         (int64_t)a->num_seqs * a->num_kv_heads <= kUnitMaxUnits;
+         (int64_t)a->num_seqs * a->num_kv_heads <= unit_max_units(cus);
 }
 // Resident multi-query waves: one per SIMD, two for FP8 pools with <= 16 columns.
-inline int mq_max_workers(int kv_dtype, int slot_cols) {
-  return (kv_dtype == PA_FP8_E4M3 && slot_cols <= 16) ? 2 * kVerifyMaxWorkers : kVerifyMaxWorkers;
+inline int mq_max_workers(int kv_dtype, int slot_cols, int cus) {
+  return (kv_dtype == PA_FP8_E4M3 && slot_cols <= 16) ? 2 * verify_max_workers(cus) : verify_max_workers(cus);
 }
 // Checks a shared-prefix decode call and resolves its three launches (prefix kernel,
 // row-part decode kernel, final merge) over the caller's workspace; with
@@ -256,6 +264,7 @@ int launch_append(const AppendLaunch &L, void *stream);
 int launch_verify_partials(const VerifyLaunch &V, void *stream);
 int launch_verify_merge(const VerifyLaunch &V, void *stream);
 int launch_cascade_merge(const CascadeMergeLaunch &M, void *stream);
+int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int num_workgroups, void *stream);
 // Auxiliary stream of the current device (streams.hip): fork makes it wait for the work
 // queued so far on main_stream; join makes main_stream wait for the work queued on it.
 int fork_side_stream(void *main_stream, void **side_stream);

@@ -122,7 +122,8 @@ __device__ int piece_tiles(const PrefillLaunch &p, int lane, int units_per_qtile
     work += __shfl_xor(work, off);
   }
   const int64_t total = work * units_per_qtile / 2;
-  const int balanced = (int)((5 * total + 4 * kPrefillSlots - 1) / (4 * kPrefillSlots));
+  const int64_t slots = p.resident_slots;
+  const int balanced = (int)((5 * total + 4 * slots - 1) / (4 * slots));
   return max(max((mx + p.splits - 1) / p.splits, balanced), kPrefillMinChunkTiles);
 }
 

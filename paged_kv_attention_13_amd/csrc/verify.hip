@@ -619,9 +619,13 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   const int qbase = ITEM == kItemDecode ? row : p.q_start_loc[row];
   const int n = ITEM == kItemDecode ? 1 : p.q_start_loc[row + 1] - qbase;
   if (c >= n * G) return;
-  const int cnt = p.seg_count[u];
+  int cnt = p.seg_count[u];
   if (cnt <= 1) return;                    // written directly by its only worker
-  const int first = p.seg_first[u];
+  // slots u + w exist for the launch's workers w in [0, num_workers): a record that does
+  // not come from the partials launch on this workspace gives wrong numbers, never a read
+  // outside it
+  const int first = min(max(p.seg_first[u], 0), p.num_workers - 1);
+  cnt = min(cnt, p.num_workers - first);
   // the pieces' maxima, one per lane: one round trip however many pieces there are
   float M = kNegBig;
   for (int base = 0; base < cnt; base += 64)

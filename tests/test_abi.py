@@ -11,10 +11,17 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "pa.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", src)))
+def _declared_functions(header=None):
+    """Functions declared in include/*.h (or in one header)."""
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in ([header] if header else sorted(os.listdir(inc))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(inc, h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -24,10 +31,10 @@ def b():
 
 
 def test_header_declares_the_calls():
-    names = _declared_functions()
+    names = _declared_functions("pa.h")
     for n in ["pa_decode", "pa_mixed", "pa_decode_plan", "pa_decode_partials", "pa_merge_partials",
               "pa_check_decode_metadata", "pa_check_mixed_metadata", "pa_mixed_workspace_size",
-              "pa_append", "pa_check_append_metadata",
+              "pa_append", "pa_check_append_metadata", "pa_decode_workspace_size", "pa_check_metadata",
               "pa_status_string", "pa_last_error", "pa_abi_version"]:
         assert n in names
 
@@ -41,7 +48,7 @@ def test_library_exports_every_declared_symbol(b):
 
 
 def test_abi_version(b):
-    assert b.LIB.pa_abi_version() == 2
+    assert b.LIB.pa_abi_version() == 3
 
 
 def test_struct_layout_matches_header(b):
@@ -552,3 +559,173 @@ def test_append_decode_metadata_checker(b):
     assert b.STATUS_NAMES[rc] == "PA_ERR_BAD_METADATA"
     slots[1] = -1                                               # a skipped token is allowed
     assert b.LIB.pa_check_append_decode_metadata(ctypes.byref(app), ctypes.byref(dec)) == 0
+
+
+def test_decode_workspace_size_is_the_plans(b):
+    """pa_decode_workspace_size returns the plan's workspace bytes (0 where no workspace is
+    needed) and SIZE_MAX, with the reason in pa_last_error, for invalid arguments."""
+    shapes = [dict(num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192),
+              dict(num_seqs=32, max_blocks_per_seq=256, max_seq_len=4096),
+              dict(num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64),          # one workgroup per unit
+              dict(num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192, num_workers=7),
+              dict(num_seqs=0)]
+    for kw in shapes:
+        a = _args(b, **kw)
+        n = b.LIB.pa_decode_workspace_size(ctypes.byref(a))
+        assert n == b.plan(a).workspace_bytes, kw
+    a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
+    assert b.LIB.pa_decode_workspace_size(ctypes.byref(a)) == 0
+    a = _args(b, kv_dtype=2, k_scale=0x10000, v_scale=0x10000, num_seqs=128, max_seq_len=8192,
+              max_blocks_per_seq=512)
+    assert b.LIB.pa_decode_workspace_size(ctypes.byref(a)) == b.plan(a).workspace_bytes > 0
+    for kw, status in [(dict(num_q_heads=30), "PA_ERR_BAD_SHAPE"), (dict(head_dim=64), "PA_ERR_UNSUPPORTED")]:
+        a = _args(b, **kw)
+        assert b.LIB.pa_decode_workspace_size(ctypes.byref(a)) == b.SIZE_MAX
+        assert b.LIB.pa_last_error().decode().startswith(status)
+        with pytest.raises(b.PagedAttentionError):
+            b.decode_workspace_bytes(a)
+    assert b.LIB.pa_decode_workspace_size(None) == b.SIZE_MAX
+
+
+def test_check_metadata_is_the_batch_validator(b):
+    """pa_check_metadata validates a whole mixed batch on host copies, like
+    pa_check_mixed_metadata, and reports the first violation."""
+    table = np.array([[0, -1, -1, -1], [1, 2, -1, -1], [3, 4, 5, -1]], np.int32)
+    lens = np.array([5, 20, 40], np.int32)
+
+    def call(qsl, fn, **kw):
+        qsl = np.asarray(qsl, np.int32)
+        m = b.MixedArgs()
+        a = m.base
+        a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = 3, 32, 8, 128
+        a.block_size, a.num_blocks, a.max_blocks_per_seq, a.max_seq_len = 16, 10, 4, 64
+        a.q_dtype = a.kv_dtype = a.out_dtype = b.PA_BF16
+        a.block_table, a.seq_lens = table.ctypes.data, lens.ctypes.data
+        m.q_start_loc, m.total_q = qsl.ctypes.data, int(qsl[-1])
+        m.num_decode_rows, m.max_q_len = 1, 40
+        for k, v in kw.items():
+            setattr(m, k, v)
+        rc = getattr(b.LIB, fn)(ctypes.byref(m))
+        return b.STATUS_NAMES[rc], b.LIB.pa_last_error().decode()
+
+    for fn in ("pa_check_metadata", "pa_check_mixed_metadata"):
+        assert call([0, 1, 9, 49], fn)[0] == "PA_OK"
+        st, msg = call([0, 2, 9, 49], fn)
+        assert st == "PA_ERR_BAD_METADATA" and "decode row" in msg
+        st, msg = call([0, 1, 30, 49], fn)
+        assert st == "PA_ERR_BAD_METADATA" and "q_len" in msg
+        st, msg = call([0, 1, 9, 49], fn, max_q_len=30)
+        assert st == "PA_ERR_BAD_METADATA" and "max_q_len" in msg
+    bad = table.copy()
+    bad[2, 1] = 10                                         # block id == num_blocks
+    table[:] = bad
+    st, msg = call([0, 1, 9, 49], "pa_check_metadata")
+    assert st == "PA_ERR_BAD_METADATA" and "outside" in msg
+    assert b.STATUS_NAMES[b.LIB.pa_check_metadata(None)] == "PA_ERR_NULL_POINTER"
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.088, float("nan"), float("inf")])
+def test_scale_must_be_positive_and_finite(b, scale):
+    """The launching calls reject a scale that is not finite and > 0 before any launch."""
+    a = _args(b, scale=scale)
+    for entry in ("pa_decode", "pa_decode_partials", "pa_merge_partials"):
+        rc = getattr(b.LIB, entry)(ctypes.byref(a), None)
+        assert b.STATUS_NAMES[rc] == "PA_ERR_UNSUPPORTED", entry
+        assert "scale" in b.LIB.pa_last_error().decode()
+    m = b.MixedArgs()
+    m.base = _args(b, scale=scale)
+    m.q_start_loc, m.total_q, m.num_decode_rows, m.max_q_len = 0x10000, 2, 2, 1
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
+    # the plan does not depend on the scale
+    assert b.plan(_args(b, scale=scale)).num_workers > 0
+
+
+def test_allocations_follow_the_launch_stream(b, monkeypatch):
+    """With an explicit stream, the output and workspace a call allocates are allocated with
+    that stream current (so torch's caching allocator ties them to it), and the launch goes to
+    that stream.  Runs on the CPU with a stand-in for torch.cuda and for the library."""
+    import types
+
+    import torch
+    events = []
+
+    class Stream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+    mine, default = Stream(0x1234), Stream(0x99)
+    current = [default]
+
+    class StreamCtx:
+        def __init__(self, s):
+            self.s = s
+
+        def __enter__(self):
+            self.prev = current[0]
+            current[0] = self.s
+
+        def __exit__(self, *e):
+            current[0] = self.prev
+            return False
+
+    def empty(*a, **kw):
+        kw["device"] = "cpu"
+        events.append(("alloc", current[0].cuda_stream))
+        return torch.empty(*a, **kw)
+
+    fake = types.SimpleNamespace(float32=torch.float32, bfloat16=torch.bfloat16, uint8=torch.uint8,
+                                 float8_e4m3fn=torch.float8_e4m3fn, empty=empty,
+                                 cuda=types.SimpleNamespace(stream=StreamCtx, current_stream=lambda: current[0]))
+
+    class Lib:
+        def pa_decode_workspace_size(self, a):
+            return 4096
+
+        def pa_mixed_workspace_size(self, m, n):
+            n._obj.value = 4096
+            return 0
+
+        def pa_cascade_workspace_size(self, c, n):
+            n._obj.value = 4096
+            return 0
+
+        def _launch(self, a, st):
+            events.append(("launch", st.value))
+            return 0
+
+        pa_decode = pa_mixed = pa_decode_cascade = _launch
+
+    monkeypatch.setattr(b, "_torch", lambda: fake)
+    monkeypatch.setattr(b, "LIB", Lib())
+    q = torch.zeros((2, 32, 128), dtype=torch.bfloat16)
+    kp = torch.zeros((4, 8, 16, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((2, 2), dtype=torch.int32)
+    sl = torch.ones(2, dtype=torch.int32)
+    qsl = torch.arange(3, dtype=torch.int32)
+    gs = torch.tensor([0, 2], dtype=torch.int32)
+    for call in (lambda st: b.decode(q, kp, kp, bt, sl, 0.1, max_seq_len=16, stream=st),
+                 lambda st: b.mixed(q, kp, kp, bt, sl, qsl, 0.1, num_decode_rows=2, max_q_len=1,
+                                    max_seq_len=16, stream=st),
+                 lambda st: b.decode_cascade(q, kp, kp, bt, sl, gs, sl, 0.1, max_seq_len=16,
+                                             max_group_rows=2, stream=st)):
+        events.clear()
+        call(mine)
+        assert events == [("alloc", 0x1234), ("alloc", 0x1234), ("launch", 0x1234)], events
+        assert current[0] is default
+        events.clear()
+        call(None)
+        assert events == [("alloc", 0x99), ("alloc", 0x99), ("launch", 0x99)], events
+
+
+def test_stream_probe_rejects_bad_arguments(b):
+    """pa_stream_read (include/pa_probe.h) validates before any launch."""
+    f = b.LIB.pa_stream_read
+    cases = [((None, 1024, 0x10000, 4), "PA_ERR_NULL_POINTER"),
+             ((0x10000, 1024, None, 4), "PA_ERR_NULL_POINTER"),
+             ((0x10008, 1024, 0x10000, 4), "PA_ERR_MISALIGNED"),
+             ((0x10000, 1000, 0x10000, 4), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 0, 0x10000, 4), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 1024, 0x10000, 0), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 1024, 0x10000, 70000), "PA_ERR_BAD_SHAPE")]
+    for args, status in cases:
+        assert b.STATUS_NAMES[f(*args, None)] == status, args
