@@ -248,6 +248,18 @@ pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes);
  * plan's one-workgroup-per-unit path take a single launch (see pa_decode_plan). */
 pa_status pa_decode(const pa_decode_args *a, void *stream);
 
+/* pa_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels,
+ * with the split partials in a fixed 16 MiB array inside the library (one per GPU,
+ * held until the process ends) instead of a caller workspace.  a->workspace and
+ * a->workspace_bytes are ignored; the caller still passes q, the pools, the metadata
+ * and out.  Calls needing more than 16 MiB of partials (pa_decode_workspace_size)
+ * return PA_ERR_WORKSPACE_TOO_SMALL before anything is launched.  Every call on one
+ * GPU uses that GPU's array, so calls that overlap on one GPU (two streams, two host
+ * threads) race and must be serialised by the caller.  No memory is allocated and
+ * nothing is synchronised; the array's device address is looked up once per device. */
+pa_status pa_decode_noalloc(const pa_decode_args *a, void *stream);
+
 /* The two stages of pa_decode, callable separately (e.g. to time one).  On the
  * one-workgroup-per-unit plan pa_decode_partials writes every output and
  * pa_merge_partials does nothing.  Otherwise pa_decode_partials writes `out`

@@ -27,7 +27,7 @@ EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_d
             "pa_check_mixed_metadata", "pa_check_append_metadata", "pa_cascade_workspace_size",
             "pa_decode_cascade", "pa_check_cascade_metadata", "pa_append_decode",
             "pa_check_append_decode_metadata", "pa_status_string", "pa_last_error",
-            "pa_decode_workspace_size", "pa_check_metadata", "pa_stream_read"]
+            "pa_decode_workspace_size", "pa_check_metadata", "pa_stream_read", "pa_decode_noalloc"]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -125,6 +125,7 @@ def _load():
         "pa_mixed_workspace_size": ([P(MixedArgs), P(ctypes.c_size_t)], ctypes.c_int),
         "pa_decode": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_decode_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
+        "pa_decode_noalloc": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_merge_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_mixed": ([P(MixedArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_append": ([P(AppendArgs), ctypes.c_void_p], ctypes.c_int),
@@ -297,6 +298,11 @@ def decode(q, k_pool, v_pool, block_table, seq_lens, scale, *, max_seq_len: int,
             a.workspace_bytes = workspace.numel() * workspace.element_size()
         check(LIB.pa_decode(ctypes.byref(a), ctypes.c_void_p(_stream(stream))))
     return out
+
+
+def decode_noalloc_args_call(args: DecodeArgs, stream=None) -> None:
+    """``pa_decode_noalloc``: pa_decode with the library's static scratch (args.workspace ignored)."""
+    check(LIB.pa_decode_noalloc(ctypes.byref(args), ctypes.c_void_p(_stream(stream))))
 
 
 def decode_partials(args: DecodeArgs, stream=None) -> None:

@@ -37,6 +37,32 @@ pa_status pa_decode_partials(const pa_decode_args *a, void *stream) {
   return hip_status(launch_decode_partials(L, stream), "decode");
 }
 
+pa_status pa_decode_noalloc(const pa_decode_args *a, void *stream) {
+  if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
+  pa_decode_args b = *a;
+  b.workspace = nullptr;                   // the caller's workspace fields are ignored
+  b.workspace_bytes = 0;
+  pa_status s = validate_decode(&b, true);
+  if (s != PA_OK) return s;
+  pa_plan plan;
+  plan_decode(&b, &plan);
+  if (plan.workspace_bytes > kStaticScratchBytes)
+    return set_error(PA_ERR_WORKSPACE_TOO_SMALL,
+                     "the call needs %zu bytes of split partials; the library's static scratch holds %zu "
+                     "(pass a workspace to pa_decode instead)",
+                     plan.workspace_bytes, kStaticScratchBytes);
+  if (b.num_seqs > 0 && plan.workspace_bytes > 0) {
+    // nothing in the scratch has to start at zero: the decode kernels write every unit's
+    // piece record and every partial that the merge reads in the same call
+    void *ptr = nullptr;
+    s = hip_status(static_scratch(&ptr), "static scratch address");
+    if (s != PA_OK) return s;
+    b.workspace = ptr;
+    b.workspace_bytes = kStaticScratchBytes;
+  }
+  return pa_decode(&b, stream);
+}
+
 pa_status pa_merge_partials(const pa_decode_args *a, void *stream) {
   pa_plan plan;
   DecodeLaunch L;

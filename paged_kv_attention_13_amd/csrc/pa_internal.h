@@ -265,6 +265,11 @@ int launch_verify_partials(const VerifyLaunch &V, void *stream);
 int launch_verify_merge(const VerifyLaunch &V, void *stream);
 int launch_cascade_merge(const CascadeMergeLaunch &M, void *stream);
 int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int num_workgroups, void *stream);
+// The library's static scratch (static_scratch.hip): 16 MiB per device, used by
+// pa_decode_noalloc in place of a caller workspace.  static_scratch() gives the current
+// device's copy's device address (looked up once per device); returns 0 or a HIP error.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+int static_scratch(void **ptr);
 // Auxiliary stream of the current device (streams.hip): fork makes it wait for the work
 // queued so far on main_stream; join makes main_stream wait for the work queued on it.
 int fork_side_stream(void *main_stream, void **side_stream);
