@@ -45,52 +45,179 @@ def parse():
                     help="CPU time budget of the oracle baseline sample (0 = skip)")
     ap.add_argument("--loop-batch", type=int, default=1,
                     help="--op loop: decode rows in the steady batch")
-    ap.add_argument("--scrub-mib", type=int, default=0,
+    ap.add_argument("--scrub-mib", type=int, default=None,
                     help="decode workloads: write this many MiB between timed steps (outside their events) "
                          "so no step reads KV left in the caches by the previous one; the step time is then "
-                         "the median of the per-step events")
+                         "the median of the per-step events.  Default: 1024 when the workload's KV bytes are "
+                         "under 1 GiB (they could otherwise stay in the 256 MB Infinity Cache and the L2s "
+                         "between steps), else 0")
+    ap.add_argument("--prewarm-ms", type=float, default=300.0,
+                    help="before the warm-up steps, run steps back to back for this long so that the GPU's "
+                         "clocks reach their sustained level (a short run otherwise times the clock ramp)")
     ap.add_argument("--prefill-case", default="w5-rows",
                     help="--op prefill: w5-rows, chunk256-after8192 or prompt8192")
     ap.add_argument("--op", default="decode",
-                    choices=["decode", "append", "append-fp8", "cascade", "loop", "prefill"],
+                    choices=["decode", "append", "append-fp8", "cascade", "loop", "prefill", "stream"],
                     help="decode: the attention call of --workload (default); append / append-fp8: "
                          "writing the mixed workload's 2,144 new tokens (96 decode + 8 x 256 prefill) "
                          "into their cache slots, bf16 -> bf16 or bf16 -> FP8-E4M3; cascade: the "
                          "shared-prefix decode call on workload 7, with pa_decode on the same rows beside it; "
                          "loop: 32 layers of append + decode per step driven by the host scheduler, launched "
-                         "eagerly and replayed as one HIP graph")
+                         "eagerly and replayed as one HIP graph; stream: the streaming-read probe over as "
+                         "many bytes as --workload's KV cache (the achievable read bandwidth)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed loop, run one device-to-device copy of this many MiB "
                          "(a plain copy kernel of known size, to calibrate HBM byte counters)")
     return ap.parse_args()
 
 
-def under_profiler() -> bool:
-    """True when a rocprofv3 tool library is preloaded into this process."""
-    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+class GpuSampler:
+    """Shader clock and board power of the GPU, sampled from sysfs in a thread while it runs.
 
-
-def gpu_state():
-    """Clock and power of the GPU right after the timed region (rocm-smi, read only), or None.
-
-    Skipped under a profiler: its preloaded library would initialise the GPU in the forked
-    child before rocm-smi's interpreter replaces it.
+    The card is the amdgpu sysfs device whose PCI slot matches torch's device 0; the current
+    shader clock is the ``pp_dpm_sclk`` level marked ``*`` and the power is hwmon's
+    ``power1_input`` (microwatts).  Only files are read: no process is started.
     """
-    import subprocess
-    if under_profiler():
-        return None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        card = next(iter(json.loads(r.stdout).values()))
-    except Exception:
-        return None
-    keep = {}
-    for k, v in card.items():
-        kl = k.lower()
-        if "sclk" in kl or "mclk" in kl or "power" in kl:
-            keep[k] = v
-    return keep or None
+
+    def __init__(self):
+        import glob
+        import torch
+        self.sclk = self.power = None
+        p = torch.cuda.get_device_properties(0)
+        slot = f"{getattr(p, 'pci_domain_id', 0):04x}:{getattr(p, 'pci_bus_id', 0):02x}:" \
+               f"{getattr(p, 'pci_device_id', 0):02x}.0"
+        for card in sorted(glob.glob("/sys/class/drm/card*")):
+            dev = os.path.join(card, "device")
+            try:
+                ok = f"PCI_SLOT_NAME={slot}" in open(os.path.join(dev, "uevent")).read()
+            except OSError:
+                continue
+            if ok and os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                self.sclk = os.path.join(dev, "pp_dpm_sclk")
+                pw = sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_input")) +
+                            glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_average")))
+                self.power = pw[0] if pw else None
+                break
+        self.samples = []
+        self._stop = False
+        self._thread = None
+
+    def _read(self):
+        import re
+        mhz = w = None
+        try:
+            for line in open(self.sclk).read().splitlines():
+                if line.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*Mhz", line, re.I)
+                    mhz = int(m.group(1)) if m else None
+            if self.power:
+                w = int(open(self.power).read().strip()) / 1e6
+        except (OSError, ValueError):
+            pass
+        return mhz, w
+
+    def _run(self):
+        while not self._stop:
+            self.samples.append(self._read())
+            time.sleep(0.0005)
+
+    def start(self):
+        import threading
+        self.samples = []
+        self._stop = False
+        if self.sclk:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self, window: str):
+        import numpy as np
+        self._stop = True
+        if self._thread:
+            self._thread.join()
+        if not self.samples:
+            return None
+        out = {"window": window, "samples": len(self.samples), "source": self.sclk}
+        for key, i in (("sclk_mhz", 0), ("power_w", 1)):
+            v = [x[i] for x in self.samples if x[i] is not None]
+            if v:
+                out[key] = {"min": round(float(np.min(v)), 1), "median": round(float(np.median(v)), 1),
+                            "max": round(float(np.max(v)), 1)}
+        return out
+
+
+STREAM_SHAPES = tuple((g, u) for g in (1024, 2048, 4096) for u in (4, 8, 16))
+
+
+def prewarm(call, ms: float) -> int:
+    """Run ``call`` back to back for ``ms`` milliseconds (synchronising every 8 calls)."""
+    import torch
+    n = 0
+    t_end = time.perf_counter() + ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
+def stream_ceiling(nbytes: int, shapes=STREAM_SHAPES, reps: int = 10, prewarm_ms: float = 100.0):
+    """Best streaming-read rate (GB/s) of ``pa_stream_read`` over ``nbytes`` bytes.
+
+    For each launch shape (workgroups, loads in flight per lane), events bracket ``reps``
+    back-to-back launches (one event pair per batch, so the pair's own cost is spread over
+    the batch); the best shape's mean is kept.
+    """
+    import torch
+    from paged_kv_attention_13_amd import binding
+    n = (nbytes + 15) // 16 * 16
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+    out = torch.empty(4 * max(g for g, _ in shapes), dtype=torch.int32, device="cuda")
+    prewarm(lambda: binding.stream_read(buf, out, shapes[0][0], shapes[0][1]), prewarm_ms)
+    res = {}
+    for g, u in shapes:
+        for _ in range(3):
+            binding.stream_read(buf, out, g, u)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            binding.stream_read(buf, out, g, u)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[(g, u)] = n / (ms * 1e-3) / 1e9
+    del buf, out
+    best = max(res, key=res.get)
+    return {"GBs": round(res[best], 1), "workgroups": best[0], "loads_in_flight": best[1], "bytes": n,
+            "per_shape_GBs": {f"{g}x{u}": round(v, 1) for (g, u), v in res.items()},
+            "load": "16-byte non-temporal loads, 256 lanes per workgroup, best launch shape"}
+
+
+def bench_stream(args):
+    """The streaming-read probe alone over the KV bytes of --workload."""
+    import pa_inputs
+    from paged_kv_attention_13_amd import accounting
+    L, _ = pa_inputs.workload_lengths(args.workload)
+    fmt = {1: "f32", 4: "fp8"}.get(args.workload, "bf16")
+    nbytes = accounting.kv_bytes(L, 8, 128, fmt)
+    sampler = GpuSampler().start()
+    st = stream_ceiling(nbytes, reps=max(10, args.steps // 5), prewarm_ms=args.prewarm_ms)
+    state = sampler.stop("the pre-warm and the timed launches")
+    print(json.dumps({
+        "metric": "streaming-read HBM GB/s (the decode kernels' load form, no compute)",
+        "value": st["GBs"], "unit": "GB/s", "n_gpus": 1, "steps": max(10, args.steps // 5), "warmup": 3,
+        "ms_per_step": round(st["bytes"] / (st["GBs"] * 1e9) * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic (constant bytes)",
+        "config": {"workload": f"stream read of {st['bytes']} bytes (the KV bytes of workload {args.workload})",
+                   "workgroups": st["workgroups"], "loads_in_flight": st["loads_in_flight"]},
+        "stream_read": st,
+        "roofline": {"bound": "hbm", "achieved": st["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(st["GBs"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "stream_read_kernel",
+                     "bytes_per_launch": st["bytes"]},
+        "cpu_baseline": None,
+        "gpu_state": state,
+    }), flush=True)
 
 
 def committed_traffic(kv_fmt: str, workload_name: str):
@@ -232,10 +359,11 @@ def bench_append(args):
     }), flush=True)
 
 
-def _timed(call, steps, warmup):
+def _timed(call, steps, warmup, prewarm_ms=0.0):
     """Mean ms per call from events around each call, and wall ms per call over the loop."""
     import numpy as np
     import torch
+    prewarm(call, prewarm_ms)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -280,8 +408,8 @@ def bench_cascade(args):
     wsd = torch.empty(max(binding.plan(a).workspace_bytes, 16), dtype=torch.uint8, device="cuda")
     a.workspace, a.workspace_bytes = wsd.data_ptr(), wsd.numel()
 
-    c_ms, c_wall = _timed(lambda: binding.cascade_args_call(c), args.steps, args.warmup)
-    d_ms, d_wall = _timed(lambda: binding.decode_args_call(a), args.steps, args.warmup)
+    c_ms, c_wall = _timed(lambda: binding.cascade_args_call(c), args.steps, args.warmup, args.prewarm_ms)
+    d_ms, d_wall = _timed(lambda: binding.decode_args_call(a), args.steps, args.warmup, args.prewarm_ms)
 
     Hkv, D = w.num_kv_heads, w.head_dim
     logical = accounting.kv_bytes(w.seq_lens, Hkv, D, "bf16")             # every row's whole cache
@@ -329,7 +457,7 @@ def bench_prefill(args):
                                 max_seq_len=w.max_seq_len, out=out)
     ws = torch.empty(max(binding.mixed_workspace_bytes(m), 16), dtype=torch.uint8, device="cuda")
     m.base.workspace, m.base.workspace_bytes = ws.data_ptr(), ws.numel()
-    c_ms, wall = _timed(lambda: binding.mixed_args_call(m), args.steps, args.warmup)
+    c_ms, wall = _timed(lambda: binding.mixed_args_call(m), args.steps, args.warmup, args.prewarm_ms)
     flops = accounting.call_flops(w.seq_lens, w.q_lens, w.num_q_heads, w.head_dim)
     ach = flops / (c_ms * 1e-3) / 1e12
     print(json.dumps({
@@ -446,6 +574,9 @@ def main():
     if args.op == "prefill":
         bench_prefill(args)
         return
+    if args.op == "stream":
+        bench_stream(args)
+        return
     if args.op != "decode":
         bench_append(args)
         return
@@ -527,6 +658,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    prewarm_steps = prewarm(run_step, args.prewarm_ms)
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -536,11 +668,15 @@ def main():
     # the merge), so the per-kernel events are recorded on every EVENT_STRIDE-th timed step only;
     # the step time is the wall clock over all timed steps.  With a scrub between steps the step
     # time is the median of per-step events instead, so every step carries them.
+    if args.scrub_mib is None:
+        args.scrub_mib = 1024 if accounting.workload_bytes(w)["kv"] < (1 << 30) else 0
     scrub = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device="cuda") if args.scrub_mib > 0 else None
     stride = 1 if scrub is not None else max(1, min(EVENT_STRIDE, args.steps // 8))
     sampled = list(range(0, args.steps, stride))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    sampler = GpuSampler()
     torch.cuda.synchronize()
+    sampler.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         if scrub is not None:
@@ -548,6 +684,7 @@ def main():
         run_step(evs.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gpu_state_summary = sampler.stop("the timed steps")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     last = 2 if two_stage else 1
     if scrub is not None:
@@ -603,7 +740,8 @@ def main():
                    "verify_rows": n_ver if mixed else 0,
                    "decode_workers": pl.num_workers if pl.num_workers and (not mixed or n_dec) else None,
                    "tile_tokens": pl.tile_tokens,
-                   "scrub_mib_between_steps": args.scrub_mib},
+                   "scrub_mib_between_steps": args.scrub_mib,
+                   "prewarm": f"{prewarm_steps} untimed steps in {args.prewarm_ms:.0f} ms before the warm-up"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(w.total_q / (ms_per_step * 1e-3), 1),
         "kv_tokens_per_s": round(float(w.seq_lens.sum()) / (ms_per_step * 1e-3), 1),
@@ -612,12 +750,16 @@ def main():
         "roofline": roofline,
         "input_generation_s": round(gen_s, 2),
     }
+    st = stream_ceiling(kv_bytes, prewarm_ms=min(100.0, args.prewarm_ms))
+    res["stream_read"] = st
+    res["pct_of_stream"] = round(100 * value / st["GBs"], 2)
+    res["kernel_pct_of_stream"] = round(100 * achieved / st["GBs"], 2)
     if args.cpu_seconds > 0:
         gpu_out = out.float().cpu().numpy().astype(np.float64)
         res["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
-    res["gpu_state_after_timing"] = gpu_state()
+    res["gpu_state"] = gpu_state_summary
     print(json.dumps(res), flush=True)
 
 

@@ -25,14 +25,17 @@ extern "C" {
 
 /* Read `bytes` bytes at `src` (a DEVICE pointer, 16-byte aligned; bytes a
  * multiple of 16) once, in num_workgroups workgroups of 256 lanes
- * (1 .. 65536) that walk it in a grid-strided loop with four loads in flight
- * per lane.  Each wave writes the XOR of the words it read to
+ * (1 .. 65536).  Workgroup w reads chunks w, w + num_workgroups, ... of
+ * 256 * loads_in_flight consecutive 16-byte vectors, each lane holding
+ * loads_in_flight (4, 8 or 16) loads in flight, then the bytes past the last
+ * whole chunk.  Each wave writes the XOR of the words it read to
  * out[4 * workgroup + wave] (a DEVICE array of 4 * num_workgroups uint32,
  * caller-owned), so the loads are not removed; the values mean nothing else.
  * Queued on `stream`; allocates nothing.  Errors: PA_ERR_NULL_POINTER,
- * PA_ERR_MISALIGNED, PA_ERR_BAD_SHAPE before any launch; PA_ERR_HIP if the
- * launch fails. */
-pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t num_workgroups, void *stream);
+ * PA_ERR_MISALIGNED, PA_ERR_BAD_SHAPE, PA_ERR_UNSUPPORTED before any launch;
+ * PA_ERR_HIP if the launch fails. */
+pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t num_workgroups,
+                         int32_t loads_in_flight, void *stream);
 
 #ifdef __cplusplus
 }

@@ -120,8 +120,8 @@ def _load():
         "pa_decode_plan": ([P(DecodeArgs), P(Plan)], ctypes.c_int),
         "pa_decode_workspace_size": ([P(DecodeArgs)], ctypes.c_size_t),
         "pa_check_metadata": ([P(MixedArgs)], ctypes.c_int),
-        "pa_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p],
-                           ctypes.c_int),
+        "pa_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                            ctypes.c_void_p], ctypes.c_int),
         "pa_mixed_workspace_size": ([P(MixedArgs), P(ctypes.c_size_t)], ctypes.c_int),
         "pa_decode": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_decode_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
@@ -516,8 +516,9 @@ def check_append_metadata(slot_mapping, *, num_kv_heads: int, head_dim: int, blo
     check(LIB.pa_check_append_metadata(ctypes.byref(a)))
 
 
-def stream_read(src, out, num_workgroups: int, stream=None) -> None:
+def stream_read(src, out, num_workgroups: int, loads_in_flight: int = 8, stream=None) -> None:
     """``pa_stream_read``: read every byte of the device tensor ``src`` once (the bandwidth
     probe); ``out`` is a device uint32/int32 tensor of 4 * num_workgroups words."""
     nbytes = src.numel() * src.element_size()
-    check(LIB.pa_stream_read(_ptr(src), nbytes, _ptr(out), int(num_workgroups), ctypes.c_void_p(_stream(stream))))
+    check(LIB.pa_stream_read(_ptr(src), nbytes, _ptr(out), int(num_workgroups), int(loads_in_flight),
+                             ctypes.c_void_p(_stream(stream))))

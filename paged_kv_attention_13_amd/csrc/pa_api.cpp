@@ -220,7 +220,8 @@ pa_status pa_decode_cascade(const pa_cascade_args *a, void *stream) {
   return hip_status(launch_cascade_merge(m, stream), "cascade merge");
 }
 
-pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t num_workgroups, void *stream) {
+pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t num_workgroups,
+                         int32_t loads_in_flight, void *stream) {
   if (!src || !out) return set_error(PA_ERR_NULL_POINTER, "src and out are required");
   if ((reinterpret_cast<uintptr_t>(src) & 15u) != 0 || (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
     return set_error(PA_ERR_MISALIGNED, "src must be 16-byte aligned and out 4-byte aligned");
@@ -228,7 +229,9 @@ pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t n
     return set_error(PA_ERR_BAD_SHAPE, "bytes=%zu must be a positive multiple of 16", bytes);
   if (num_workgroups < 1 || num_workgroups > 65536)
     return set_error(PA_ERR_BAD_SHAPE, "num_workgroups=%d outside [1, 65536]", num_workgroups);
-  return hip_status(launch_stream_read(src, bytes, out, num_workgroups, stream), "stream read");
+  if (loads_in_flight != 4 && loads_in_flight != 8 && loads_in_flight != 16)
+    return set_error(PA_ERR_UNSUPPORTED, "loads_in_flight=%d (supported: 4, 8, 16)", loads_in_flight);
+  return hip_status(launch_stream_read(src, bytes, out, num_workgroups, loads_in_flight, stream), "stream read");
 }
 
 }  // extern "C"

@@ -264,7 +264,8 @@ int launch_append(const AppendLaunch &L, void *stream);
 int launch_verify_partials(const VerifyLaunch &V, void *stream);
 int launch_verify_merge(const VerifyLaunch &V, void *stream);
 int launch_cascade_merge(const CascadeMergeLaunch &M, void *stream);
-int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int num_workgroups, void *stream);
+int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int num_workgroups, int loads_in_flight,
+                       void *stream);
 // The library's static scratch (static_scratch.hip): 16 MiB per device, used by
 // pa_decode_noalloc in place of a caller workspace.  static_scratch() gives the current
 // device's copy's device address (looked up once per device); returns 0 or a HIP error.

@@ -13,19 +13,23 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ unsigned fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
+// Workgroup w reads chunks w, w + grid, ... of kThreads * U consecutive 16-byte vectors,
+// U loads in flight per lane (lane l takes vectors l, l + 256, ...: each load instruction
+// covers 4 KB of consecutive bytes), then the vectors past the last whole chunk.
+template <int U>
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4 *src, size_t n, unsigned *out) {
-  const size_t stride = (size_t)gridDim.x * kThreads;
-  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr size_t kChunk = (size_t)kThreads * U;
+  const size_t whole = n / kChunk * kChunk;
   unsigned acc = 0;
-  // four independent loads in flight per lane
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
+  for (size_t base = (size_t)blockIdx.x * kChunk; base < whole; base += (size_t)gridDim.x * kChunk) {
+    u32x4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) v[k] = __builtin_nontemporal_load(src + base + k * kThreads + threadIdx.x);
+#pragma unroll
+    for (int k = 0; k < U; ++k) acc ^= fold(v[k]);
   }
-  for (; i < n; i += stride) acc ^= fold(__builtin_nontemporal_load(src + i));
+  for (size_t i = whole + (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
+    acc ^= fold(__builtin_nontemporal_load(src + i));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off);
   if ((threadIdx.x & 63) == 0) out[blockIdx.x * (kThreads / 64) + threadIdx.x / 64] = acc;
@@ -36,9 +40,18 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4 *src,
 
 namespace pa {
 
-int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int num_workgroups, void *stream) {
-  hipLaunchKernelGGL(stream_read_kernel, dim3(num_workgroups), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4 *>(src), bytes / 16, reinterpret_cast<unsigned *>(out));
+int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int num_workgroups, int loads_in_flight,
+                       void *stream) {
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4 *s = static_cast<const u32x4 *>(src);
+  unsigned *o = reinterpret_cast<unsigned *>(out);
+  const size_t n = bytes / 16;
+  if (loads_in_flight == 4)
+    hipLaunchKernelGGL(stream_read_kernel<4>, dim3(num_workgroups), dim3(kThreads), 0, st, s, n, o);
+  else if (loads_in_flight == 8)
+    hipLaunchKernelGGL(stream_read_kernel<8>, dim3(num_workgroups), dim3(kThreads), 0, st, s, n, o);
+  else
+    hipLaunchKernelGGL(stream_read_kernel<16>, dim3(num_workgroups), dim3(kThreads), 0, st, s, n, o);
   return (int)hipGetLastError();
 }
 

@@ -720,12 +720,13 @@ def test_allocations_follow_the_launch_stream(b, monkeypatch):
 def test_stream_probe_rejects_bad_arguments(b):
     """pa_stream_read (include/pa_probe.h) validates before any launch."""
     f = b.LIB.pa_stream_read
-    cases = [((None, 1024, 0x10000, 4), "PA_ERR_NULL_POINTER"),
-             ((0x10000, 1024, None, 4), "PA_ERR_NULL_POINTER"),
-             ((0x10008, 1024, 0x10000, 4), "PA_ERR_MISALIGNED"),
-             ((0x10000, 1000, 0x10000, 4), "PA_ERR_BAD_SHAPE"),
-             ((0x10000, 0, 0x10000, 4), "PA_ERR_BAD_SHAPE"),
-             ((0x10000, 1024, 0x10000, 0), "PA_ERR_BAD_SHAPE"),
-             ((0x10000, 1024, 0x10000, 70000), "PA_ERR_BAD_SHAPE")]
+    cases = [((None, 1024, 0x10000, 4, 8), "PA_ERR_NULL_POINTER"),
+             ((0x10000, 1024, None, 4, 8), "PA_ERR_NULL_POINTER"),
+             ((0x10008, 1024, 0x10000, 4, 8), "PA_ERR_MISALIGNED"),
+             ((0x10000, 1000, 0x10000, 4, 8), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 0, 0x10000, 4, 8), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 1024, 0x10000, 0, 8), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 1024, 0x10000, 70000, 8), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 1024, 0x10000, 4, 5), "PA_ERR_UNSUPPORTED")]
     for args, status in cases:
         assert b.STATUS_NAMES[f(*args, None)] == status, args
