@@ -127,6 +127,45 @@ __device__ int piece_tiles(const PrefillLaunch &p, int lane, int units_per_qtile
   return max(max((mx + p.splits - 1) / p.splits, balanced), kPrefillMinChunkTiles);
 }
 
+// The unit of one prefill workgroup.  Workgroups are dispatched to the 8 XCDs round-robin
+// (id mod 8), each XCD with its own L2; when the (kv head, head block) pairs come in
+// multiples of 8, all workgroups of a pair go to one XCD, so that XCD's L2 serves the K/V
+// tiles every query tile of the pair re-reads (8 kv heads: one per XCD).  Then the query
+// tile, the longest (last in the row) dispatched first, then (piece, row) with the piece
+// slowest, so consecutive workgroups are different units rather than pieces of one unit
+// that may have no work.
+struct PrefillUnit {
+  int qt;          // query tile
+  int piece;       // kv piece
+  int row_local;   // prefill row, from first_row
+  int g;           // kv head
+  int hb;          // head block within the kv head
+  int hbk;         // (kv head, head block) pair
+};
+
+__device__ __forceinline__ PrefillUnit prefill_unit(const PrefillLaunch &p, int hblocks) {
+  const int U = p.num_kv_heads * hblocks;
+  const int id = (int)blockIdx.x;
+  int hbk, rest;
+  if (U % 8 == 0) {
+    const int k = id >> 3;
+    hbk = (id & 7) + 8 * (k % (U >> 3));
+    rest = k / (U >> 3);
+  } else {
+    hbk = id % U;
+    rest = id / U;
+  }
+  PrefillUnit u;
+  u.qt = p.max_qtiles - 1 - rest % p.max_qtiles;
+  const int zz = rest / p.max_qtiles;
+  u.piece = zz / p.num_rows;
+  u.row_local = zz % p.num_rows;
+  u.g = hbk / hblocks;
+  u.hb = hbk % hblocks;
+  u.hbk = hbk;
+  return u;
+}
+
 // HB: query heads per workgroup (1, 2 or 4); the 4 waves cover HB heads x (4/HB) query sub-tiles.
 template <int HB, bool OUT_BF16>
 __global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -143,14 +182,14 @@ void prefill_kernel(PrefillLaunch p) {
   const int Hkv = p.num_kv_heads;
   const int G = Hq / Hkv;
   const int hblocks = G / HB;              // head blocks per kv head
-  // x: query tile, the longest (last in the row) dispatched first; z: (piece, row) with the
-  // piece slowest, so consecutive workgroups (spread round-robin over the XCDs) are
-  // different units rather than pieces of one unit that may have no work
-  const int qt = p.max_qtiles - 1 - (int)blockIdx.x;
-  const int piece = (int)blockIdx.z / p.num_rows;
-  const int row_local = (int)blockIdx.z % p.num_rows;
-  const int g = blockIdx.y / hblocks;
-  const int hb = blockIdx.y % hblocks;
+  const int U = Hkv * hblocks;             // (kv head, head block) pairs
+  const PrefillUnit un = prefill_unit(p, hblocks);
+  const int qt = un.qt;
+  const int piece = un.piece;
+  const int row_local = un.row_local;
+  const int g = un.g;
+  const int hb = un.hb;
+  const int hbk = un.hbk;
   const int row = p.first_row + row_local;
   const int q_begin = p.q_start_loc[row];
   const int n = p.q_start_loc[row + 1] - q_begin;
@@ -407,8 +446,7 @@ void prefill_kernel(PrefillLaunch p) {
     // a piece of a cut unit: the unnormalised sum, the running max and the sum of
     // weights go to the piece's slot (a wave that saw no tile of this piece leaves
     // max = -1e30, sum = 0, zeros); the merge kernel combines the pieces
-    const size_t slot = ((((size_t)row_local * gridDim.y + blockIdx.y) * p.max_qtiles + qt) * p.splits +
-                         piece) * NWP + wave;
+    const size_t slot = ((((size_t)row_local * U + hbk) * p.max_qtiles + qt) * p.splits + piece) * NWP + wave;
     float *po = p.part_o + slot * (QW * D);
     float *pml = p.part_ml + slot * (QW * 2);
 #pragma unroll
@@ -536,7 +574,11 @@ int launch_hb(const PrefillLaunch &P, hipStream_t st) {
   if (P.max_qtiles != (P.max_q_len + QB - 1) / QB || P.splits < 1 || P.splits > kPrefillMaxSplits ||
       (P.splits > 1 && (!P.part_o || !P.part_ml)))
     return (int)hipErrorInvalidValue;
-  dim3 grid(P.max_qtiles, P.num_kv_heads * (G / HB), P.num_rows * P.splits);
+  // one-dimensional grid of (query tiles) x (kv head, head block) x (rows x pieces); the
+  // kernel decodes its unit from the workgroup id (prefill_unit)
+  const int64_t nwg = (int64_t)P.max_qtiles * P.num_kv_heads * (G / HB) * P.num_rows * P.splits;
+  if (nwg > INT32_MAX) return (int)hipErrorInvalidValue;
+  dim3 grid((unsigned)nwg);
   if (P.out_dtype == PA_BF16)
     hipLaunchKernelGGL((prefill_kernel<HB, true>), grid, dim3(NTP), 0, st, P);
   else

@@ -42,10 +42,12 @@ def test_prefill_only_f32_out():
     compare(got, ref, 1e-2, what="prefill f32 out")
 
 
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8)])
-def test_prefill_group_sizes(hq, hkv):
-    _announce(f"prefill group hq={hq} hkv={hkv}")
-    w = _mixed([33], [(0, 40), (70, 100), (5, 200)], hq=hq, hkv=hkv, seed=hq)
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (64, 8), (32, 8)])
+@pytest.mark.parametrize("dec", [[33], []])
+def test_prefill_group_sizes(hq, hkv, dec):
+    """Every group size, beside a decode row (prefill on the auxiliary stream) and alone."""
+    _announce(f"prefill group hq={hq} hkv={hkv} decode rows {dec}")
+    w = _mixed(dec, [(0, 40), (70, 100), (5, 200), (300, 333)], hq=hq, hkv=hkv, seed=hq + len(dec))
     ref = oracle.paged_attention_workload(w)
     got = run_mixed(w, out_dtype="f32")
     compare(got, ref, 1e-2, what=f"prefill G={hq // hkv}")
@@ -92,7 +94,8 @@ def test_prefill_split_matches_unsplit():
     from paged_kv_attention_13_amd.device import to_device
     d = to_device(w)
     out = binding.mixed(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], d["q_start_loc"],
-                        w.scale, num_decode_rows=0, max_q_len=1024, max_seq_len=w.max_seq_len, out_dtype=torch.float32)
+                        w.scale, num_decode_rows=0, max_q_len=w.max_seq_len, max_seq_len=w.max_seq_len,
+                        out_dtype=torch.float32)
     torch.cuda.synchronize()
     got_one = out.cpu().numpy().astype(np.float64)
     compare(got_one, ref, 1e-2, what="prefill in one pass")
@@ -100,10 +103,12 @@ def test_prefill_split_matches_unsplit():
 
 
 @pytest.mark.parametrize("bs", [32, 128])
-def test_prefill_pieces_start_mid_page(bs):
-    """Pieces of 64-token tiles over 128-token pages start in the middle of a page."""
-    _announce(f"prefill pieces, bs={bs}")
-    w = _mixed([], [(5000, 40), (700, 300)], bs=bs, seed=47 + bs)
+@pytest.mark.parametrize("dec", [[], [77]])
+def test_prefill_pieces_start_mid_page(bs, dec):
+    """Pieces of 64-token tiles over 128-token pages start in the middle of a page, with the
+    prefill rows alone and beside a decode row."""
+    _announce(f"prefill pieces, bs={bs}, decode rows {dec}")
+    w = _mixed(dec, [(5000, 40), (700, 300)], bs=bs, seed=47 + bs)
     ref = oracle.paged_attention_workload(w)
     got = run_mixed(w, out_dtype="f32")
     compare(got, ref, 1e-2, what=f"prefill pieces bs{bs}")

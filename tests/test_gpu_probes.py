@@ -91,12 +91,14 @@ def test_verify_probes(kv_fmt, bs, workers):
 
 
 @pytest.mark.parametrize("bs", [16, 64])
-@pytest.mark.parametrize("workers", [0, 37])
+@pytest.mark.parametrize("workers", [0, 37, None])
 def test_mixed_prefill_probes(bs, workers):
     """Decode rows plus prefill-chunk rows whose kv pieces start in the middle of a page
-    (few units: the launch cuts long units into pieces), with the diagonal among the targets."""
+    (few units: the launch cuts long units into pieces), with the diagonal among the targets.
+    workers None: the prefill rows alone."""
     _announce(f"prefill probes bs={bs} workers={workers}")
-    dec = [1, 300, 3000]
+    dec = [1, 300, 3000] if workers is not None else []
+    workers = workers or 0
     pre = [(0, 64), (100, 256), (1000, 40), (37, 5), (2500, 33)]
     w = _workload(dec + [p + n for p, n in pre], [1] * len(dec) + [n for _, n in pre], bs=bs, seed=bs + workers + 9)
     _sweep(w, lambda w, d: run_mixed(w, out_dtype="f32", num_workers=workers, dev=d),
@@ -148,6 +150,14 @@ def test_full_size_probes(i):
     _sweep(w, run, probe=probe, launches=2, what=f"workload {i}")
 
 
+@pytest.mark.parametrize("case", ["w5-rows", "chunk256-after8192"])
+def test_full_size_prefill_rows_probes(case):
+    """Prefill rows alone at full size (kv pieces for the single chunk after 8,192 tokens)."""
+    _announce(f"full-size prefill probes: {case}")
+    w = pa_inputs.make_prefill_case(case)
+    _sweep(w, lambda w, d: run_mixed(w, dev=d), launches=2, what=f"prefill {case}")
+
+
 # ----------------------------------------------------------------------------
 # physical-block permutation: bit-identical outputs
 # ----------------------------------------------------------------------------
@@ -174,9 +184,9 @@ def test_fp8_decode_block_permutation_bit_identical(bs, workers):
 
 
 @pytest.mark.parametrize("bs", [16, 64])
-def test_prefill_block_permutation_bit_identical(bs):
-    _announce(f"mixed prefill block permutation bs={bs}")
-    dec = [1, 300, 3000]
+@pytest.mark.parametrize("dec", [[1, 300, 3000], []])
+def test_prefill_block_permutation_bit_identical(bs, dec):
+    _announce(f"prefill block permutation bs={bs} decode rows {dec}")
     pre = [(0, 64), (100, 256), (1000, 40), (2500, 33)]
     w = _workload(dec + [p + n for p, n in pre], [1] * len(dec) + [n for _, n in pre], bs=bs, seed=400 + bs)
     a = run_mixed(w)
