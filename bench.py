@@ -46,11 +46,11 @@ def parse():
     ap.add_argument("--loop-batch", type=int, default=1,
                     help="--op loop: decode rows in the steady batch")
     ap.add_argument("--scrub-mib", type=int, default=None,
-                    help="decode workloads: write this many MiB between timed steps (outside their events) "
-                         "so no step reads KV left in the caches by the previous one; the step time is then "
-                         "the median of the per-step events.  Default: 1024 when the workload's KV bytes are "
-                         "under 1 GiB (they could otherwise stay in the 256 MB Infinity Cache and the L2s "
-                         "between steps), else 0")
+                    help="decode workloads: read this many MiB between timed steps (outside their events, "
+                         "with cache-allocating loads) so no step reads KV left in the caches by the previous "
+                         "one; the step time is then the median of the per-step events.  Default: 1024 when "
+                         "the workload's KV bytes are under 1 GiB (they could otherwise stay in the 256 MB "
+                         "Infinity Cache and the L2s between steps), else 0")
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="before the warm-up steps, run steps back to back for this long so that the GPU's "
                          "clocks reach their sustained level (a short run otherwise times the clock ramp)")
@@ -192,6 +192,53 @@ def stream_ceiling(nbytes: int, shapes=STREAM_SHAPES, reps: int = 10, prewarm_ms
     return {"GBs": round(res[best], 1), "workgroups": best[0], "loads_in_flight": best[1], "bytes": n,
             "per_shape_GBs": {f"{g}x{u}": round(v, 1) for (g, u), v in res.items()},
             "load": "16-byte non-temporal loads, 256 lanes per workgroup, best launch shape"}
+
+
+GATHER_SHAPES = tuple((g, f) for g in (256, 512, 1024, 2048) for f in (2, 4, 8))
+
+
+def gather_ceiling(w, d, shapes=GATHER_SHAPES, reps: int = 10, prewarm_ms: float = 100.0):
+    """Best rate (GB/s) of ``pa_gather_read`` over the pages a decode call of workload ``w``
+    visits -- every (block, kv head) page of K and of V of every row, in the decode kernels'
+    order (row, kv head, block) -- at the workload's own page size."""
+    import numpy as np
+    import torch
+    from paged_kv_attention_13_amd import binding
+    kp, vp = d["k_pool"], d["v_pool"]
+    elem = kp.element_size()
+    page = w.block_size * w.head_dim * elem
+    base = min(kp.data_ptr(), vp.data_ptr())
+    offs = []
+    for b in range(w.num_seqs):
+        nblk = (int(w.seq_lens[b]) + w.block_size - 1) // w.block_size
+        phys = w.block_table[b, :nblk].astype(np.int64)
+        for g in range(w.num_kv_heads):
+            pg = (phys * w.num_kv_heads + g) * page
+            kv = np.empty(2 * nblk, np.int64)
+            kv[0::2] = kp.data_ptr() - base + pg
+            kv[1::2] = vp.data_ptr() - base + pg
+            offs.append(kv)
+    offs = torch.from_numpy(np.concatenate(offs)).cuda()
+    basev = kp if kp.data_ptr() == base else vp
+    out = torch.empty(4 * max(g for g, _ in shapes), dtype=torch.int32, device="cuda")
+    nbytes = offs.numel() * page
+    prewarm(lambda: binding.gather_read(basev, offs, page, out, shapes[0][0], shapes[0][1]), prewarm_ms)
+    res = {}
+    for g, f in shapes:
+        for _ in range(3):
+            binding.gather_read(basev, offs, page, out, g, f)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            binding.gather_read(basev, offs, page, out, g, f)
+        e1.record()
+        torch.cuda.synchronize()
+        res[(g, f)] = nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+    best = max(res, key=res.get)
+    return {"GBs": round(res[best], 1), "workgroups": best[0], "pages_in_flight": best[1], "page_bytes": page,
+            "pages": int(offs.numel()), "bytes": int(nbytes),
+            "per_shape_GBs": {f"{g}x{f}": round(v, 1) for (g, f), v in res.items()},
+            "load": "whole (block, kv head) pages in decode order, 16-byte non-temporal loads, best launch shape"}
 
 
 def bench_stream(args):
@@ -670,7 +717,10 @@ def main():
     # time is the median of per-step events instead, so every step carries them.
     if args.scrub_mib is None:
         args.scrub_mib = 1024 if accounting.workload_bytes(w)["kv"] < (1 << 30) else 0
-    scrub = torch.empty(args.scrub_mib << 20, dtype=torch.uint8, device="cuda") if args.scrub_mib > 0 else None
+    # the scrub reads (it does not write): a write would leave the caches full of dirty lines
+    # whose write-back then competes with the next step's reads
+    scrub = torch.ones((args.scrub_mib << 20) // 4, dtype=torch.int32, device="cuda") if args.scrub_mib > 0 else None
+    scrub_out = torch.empty((), dtype=torch.int32, device="cuda")
     stride = 1 if scrub is not None else max(1, min(EVENT_STRIDE, args.steps // 8))
     sampled = list(range(0, args.steps, stride))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
@@ -680,7 +730,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         if scrub is not None:
-            scrub.fill_(i & 255)
+            torch.amax(scrub, dim=0, out=scrub_out)
         run_step(evs.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -754,6 +804,11 @@ def main():
     res["stream_read"] = st
     res["pct_of_stream"] = round(100 * value / st["GBs"], 2)
     res["kernel_pct_of_stream"] = round(100 * achieved / st["GBs"], 2)
+    if not mixed:
+        gt = gather_ceiling(w, d, prewarm_ms=min(100.0, args.prewarm_ms))
+        res["gather_read"] = gt
+        res["pct_of_gather"] = round(100 * value / gt["GBs"], 2)
+        res["kernel_pct_of_gather"] = round(100 * achieved / gt["GBs"], 2)
     if args.cpu_seconds > 0:
         gpu_out = out.float().cpu().numpy().astype(np.float64)
         res["cpu_baseline"] = cpu_baseline(w, gpu_out, args.cpu_seconds)

@@ -37,6 +37,21 @@ extern "C" {
 pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t num_workgroups,
                          int32_t loads_in_flight, void *stream);
 
+/* The same for paged reads: read num_pages pages of page_bytes bytes (a positive
+ * multiple of 1024) at base + page_offsets[i] (DEVICE pointers: base 16-byte aligned,
+ * page_offsets an int64 array of byte offsets, each a multiple of 16, the pages inside
+ * the caller's allocation), in list order.  The list is cut into equal contiguous
+ * ranges, one per wave (4 waves per workgroup), each lane loading 16 bytes of every
+ * kilobyte with pages_in_flight (2, 4 or 8) pages in flight -- the decode kernels'
+ * pattern: a request's
+ * blocks gathered through its table, one (block, kv head) page at a time ("How does
+ * TensorRT-LLM work" (outcomeschool.com), section "The paged KV cache").  With the
+ * pages a decode call visits, in its order, the rate is the achievable bandwidth of
+ * that access pattern (pages of a few KB at random physical places).  out: 4 *
+ * num_workgroups uint32, as for pa_stream_read.  Same errors. */
+pa_status pa_gather_read(const void *base, const int64_t *page_offsets, int64_t num_pages, int32_t page_bytes,
+                         uint32_t *out, int32_t num_workgroups, int32_t pages_in_flight, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_d
             "pa_check_mixed_metadata", "pa_check_append_metadata", "pa_cascade_workspace_size",
             "pa_decode_cascade", "pa_check_cascade_metadata", "pa_append_decode",
             "pa_check_append_decode_metadata", "pa_status_string", "pa_last_error",
-            "pa_decode_workspace_size", "pa_check_metadata", "pa_stream_read", "pa_decode_noalloc"]
+            "pa_decode_workspace_size", "pa_check_metadata", "pa_stream_read", "pa_decode_noalloc",
+            "pa_gather_read"]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -122,6 +123,8 @@ def _load():
         "pa_check_metadata": ([P(MixedArgs)], ctypes.c_int),
         "pa_stream_read": ([ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                             ctypes.c_void_p], ctypes.c_int),
+        "pa_gather_read": ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p], ctypes.c_int),
         "pa_mixed_workspace_size": ([P(MixedArgs), P(ctypes.c_size_t)], ctypes.c_int),
         "pa_decode": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
         "pa_decode_partials": ([P(DecodeArgs), ctypes.c_void_p], ctypes.c_int),
@@ -522,3 +525,11 @@ def stream_read(src, out, num_workgroups: int, loads_in_flight: int = 8, stream=
     nbytes = src.numel() * src.element_size()
     check(LIB.pa_stream_read(_ptr(src), nbytes, _ptr(out), int(num_workgroups), int(loads_in_flight),
                              ctypes.c_void_p(_stream(stream))))
+
+
+def gather_read(base, page_offsets, page_bytes: int, out, num_workgroups: int, pages_in_flight: int = 4,
+                stream=None) -> None:
+    """``pa_gather_read``: read the pages ``base + page_offsets[i]`` (an int64 device tensor of
+    byte offsets) of ``page_bytes`` each, in list order (the paged-read bandwidth probe)."""
+    check(LIB.pa_gather_read(_ptr(base), _ptr(page_offsets), int(page_offsets.numel()), int(page_bytes),
+                             _ptr(out), int(num_workgroups), int(pages_in_flight), ctypes.c_void_p(_stream(stream))))

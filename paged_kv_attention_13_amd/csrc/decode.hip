@@ -219,6 +219,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   int tv = (int)((x0 - rowstart) % vnb);
   long long ustart = rowstart + (long long)g * vnb;
   long long x = x0;
+  int tbl0 = 0, tbl0_row = -1;             // the first 64 block-table entries of row tbl0_row
 
   while (x < x1) {
     const int cntv = (int)min((long long)(vnb - tv), x1 - x);
@@ -464,10 +465,20 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
       }
     };
     // walk the segment in chunks of 64 pages (one block-table load per chunk); chunk
-    // boundaries fall on multiples of 64 pages, which are tile boundaries
+    // boundaries fall on multiples of 64 pages, which are tile boundaries.  The row's
+    // first chunk is kept across units: the next unit is usually the next kv head of the
+    // same row, which then starts without waiting for a table load.
     for (int ta = 0; ta < cnt;) {
       const int tb = min(cnt, (((chunk_base + 64) << log2bs) - tok_begin) / TILE);
-      tbl = trow[min(chunk_base + lane, mb_last)];
+      if (chunk_base == 0 && b == tbl0_row) {
+        tbl = tbl0;
+      } else {
+        tbl = trow[min(chunk_base + lane, mb_last)];
+        if (chunk_base == 0) {
+          tbl0 = tbl;
+          tbl0_row = b;
+        }
+      }
       run_tiles(ta, tb);
       ta = tb;
       chunk_base += 64;

@@ -18,6 +18,7 @@ int launch_verify_partials(const VerifyLaunch &, void *) { return kNoDevice; }
 int launch_verify_merge(const VerifyLaunch &, void *) { return kNoDevice; }
 int launch_cascade_merge(const CascadeMergeLaunch &, void *) { return kNoDevice; }
 int launch_stream_read(const void *, size_t, uint32_t *, int, int, void *) { return kNoDevice; }
+int launch_gather_read(const void *, const int64_t *, long long, int, uint32_t *, int, int, void *) { return kNoDevice; }
 int fork_side_stream(void *, void **) { return kNoDevice; }
 int static_scratch(void **) { return kNoDevice; }
 int join_side_stream(void *) { return kNoDevice; }

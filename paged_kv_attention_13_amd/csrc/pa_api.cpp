@@ -234,4 +234,22 @@ pa_status pa_stream_read(const void *src, size_t bytes, uint32_t *out, int32_t n
   return hip_status(launch_stream_read(src, bytes, out, num_workgroups, loads_in_flight, stream), "stream read");
 }
 
+pa_status pa_gather_read(const void *base, const int64_t *page_offsets, int64_t num_pages, int32_t page_bytes,
+                         uint32_t *out, int32_t num_workgroups, int32_t pages_in_flight, void *stream) {
+  if (!base || !page_offsets || !out) return set_error(PA_ERR_NULL_POINTER, "base, page_offsets and out are required");
+  if ((reinterpret_cast<uintptr_t>(base) & 15u) != 0 || (reinterpret_cast<uintptr_t>(page_offsets) & 7u) != 0 ||
+      (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+    return set_error(PA_ERR_MISALIGNED, "base must be 16-byte, page_offsets 8-byte and out 4-byte aligned");
+  if (num_pages < 1 || page_bytes < 1024 || page_bytes % 1024 != 0)
+    return set_error(PA_ERR_BAD_SHAPE, "num_pages=%lld must be >= 1 and page_bytes=%d a positive multiple of 1024",
+                     (long long)num_pages, page_bytes);
+  if (num_workgroups < 1 || num_workgroups > 65536)
+    return set_error(PA_ERR_BAD_SHAPE, "num_workgroups=%d outside [1, 65536]", num_workgroups);
+  if (pages_in_flight != 2 && pages_in_flight != 4 && pages_in_flight != 8)
+    return set_error(PA_ERR_UNSUPPORTED, "pages_in_flight=%d (supported: 2, 4, 8)", pages_in_flight);
+  return hip_status(launch_gather_read(base, page_offsets, num_pages, page_bytes, out, num_workgroups,
+                                       pages_in_flight, stream),
+                    "gather read");
+}
+
 }  // extern "C"

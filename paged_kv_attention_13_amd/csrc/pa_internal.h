@@ -266,6 +266,8 @@ int launch_verify_merge(const VerifyLaunch &V, void *stream);
 int launch_cascade_merge(const CascadeMergeLaunch &M, void *stream);
 int launch_stream_read(const void *src, size_t bytes, uint32_t *out, int num_workgroups, int loads_in_flight,
                        void *stream);
+int launch_gather_read(const void *base, const int64_t *offsets, long long npages, int page_bytes, uint32_t *out,
+                       int num_workgroups, int pages_in_flight, void *stream);
 // The library's static scratch (static_scratch.hip): 16 MiB per device, used by
 // pa_decode_noalloc in place of a caller workspace.  static_scratch() gives the current
 // device's copy's device address (looked up once per device); returns 0 or a HIP error.

@@ -267,6 +267,7 @@ void verify_kernel(VerifyLaunch p) {
   int tv = (int)((x0 - rowstart) % vnb);
   long long ustart = rowstart + (long long)g * vnb;
   long long x = x0;
+  int tbl0 = 0, tbl0_row = -1;             // the first 64 block-table entries of row tbl0_row
 
   while (x < x1) {
     const int cntv = (int)min((long long)(vnb - tv), x1 - x);
@@ -546,10 +547,19 @@ void verify_kernel(VerifyLaunch p) {
         if (t + 2 < tb) compute_tile(t + 2, kc, vc);
       }
     };
-    // chunks of 64 pages share one block-table load (64 * bs tokens: whole tiles)
+    // chunks of 64 pages share one block-table load (64 * bs tokens: whole tiles); the
+    // row's first chunk is kept for the next unit, usually the next kv head of the row
     for (int ta = 0; ta < cnt;) {
       const int tb = min(cnt, (((chunk_base + 64) << log2bs) - tok_begin) / TILE);
-      tbl = trow[min(chunk_base + lane, mb_last)];
+      if (chunk_base == 0 && row == tbl0_row) {
+        tbl = tbl0;
+      } else {
+        tbl = trow[min(chunk_base + lane, mb_last)];
+        if (chunk_base == 0) {
+          tbl0 = tbl;
+          tbl0_row = row;
+        }
+      }
       run_tiles(ta, tb);
       ta = tb;
       chunk_base += 64;

@@ -730,3 +730,17 @@ def test_stream_probe_rejects_bad_arguments(b):
              ((0x10000, 1024, 0x10000, 4, 5), "PA_ERR_UNSUPPORTED")]
     for args, status in cases:
         assert b.STATUS_NAMES[f(*args, None)] == status, args
+
+
+def test_gather_probe_rejects_bad_arguments(b):
+    f = b.LIB.pa_gather_read
+    cases = [((None, 0x10000, 4, 2048, 0x10000, 4, 4), "PA_ERR_NULL_POINTER"),
+             ((0x10000, None, 4, 2048, 0x10000, 4, 4), "PA_ERR_NULL_POINTER"),
+             ((0x10008, 0x10000, 4, 2048, 0x10000, 4, 4), "PA_ERR_MISALIGNED"),
+             ((0x10000, 0x10004, 4, 2048, 0x10000, 4, 4), "PA_ERR_MISALIGNED"),
+             ((0x10000, 0x10000, 0, 2048, 0x10000, 4, 4), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 0x10000, 4, 1000, 0x10000, 4, 4), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 0x10000, 4, 2048, 0x10000, 0, 4), "PA_ERR_BAD_SHAPE"),
+             ((0x10000, 0x10000, 4, 2048, 0x10000, 4, 3), "PA_ERR_UNSUPPORTED")]
+    for args, status in cases:
+        assert b.STATUS_NAMES[f(*args, None)] == status, args
