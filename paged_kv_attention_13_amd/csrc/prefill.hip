@@ -281,11 +281,13 @@ void prefill_kernel(PrefillLaunch p) {
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i)
       *reinterpret_cast<u32x4 *>(kb + (4 * c_tq + i) * K_STRIDE + c_dg * 16) = rk[i];
-    // V^T: for element d = 8*dg + e, the 4 tokens 4*tq .. +3 become one 8-byte group of row d,
-    // stored at group tq ^ ((d >> 3) & 11): an XOR swizzle that leaves bit 2 of the group alone,
-    // so an operand's low token group always sits 32 bytes below its high one (one paired
-    // read, no register reordering); conflict-free loads, 2-way conflicts on the stores
-    const int vgrp = 8 * (c_tq ^ (c_dg & 11));
+    // V^T: for element d = 8*dg + e, the 4 tokens 4*tq .. +3 become one 8-byte half of row d's
+    // 16-byte pair 4*(tq >> 3) + (tq & 3) (low half for tq & 4 clear): a pair holds an MFMA
+    // operand's 8 k slots in order, so each operand is one 16-byte read (gfx950 serves
+    // 16-byte LDS reads at twice the bytes per clock of 8-byte ones).  Pairs are XOR-ed with
+    // (d >> 4) & 7, the operand's 16-row block: conflict-free operand reads, two-way
+    // conflicted stores under a 64-bank model.
+    const int vgrp = 16 * ((4 * (c_tq >> 3) + (c_tq & 3)) ^ ((c_dg >> 1) & 7)) + 8 * ((c_tq >> 2) & 1);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t lo01 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x05040100u);   // e=2w:   t0 t1
@@ -305,10 +307,11 @@ void prefill_kernel(PrefillLaunch p) {
     for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = f32x4{0.f, 0.f, 0.f, 0.f};
   float lsum[2] = {0.f, 0.f};              // per-lane partial of the softmax denominator
 
-  // lane parts of the V^T operand addresses (see the product below)
-  const int vt_lane = lq * V_STRIDE + 8 * ((lg & 1) ^ (lq >> 3));
-  const int vt_lane_even = vt_lane + 16 * ((lg >> 1) & 1);
-  const int vt_lane_odd = vt_lane + 16 * (((lg >> 1) & 1) ^ 1);
+  // lane parts of the V^T operand addresses: row lq of a 16-row block, pair lg ^ i (see the
+  // product below)
+  int vt_lane[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vt_lane[i] = lq * V_STRIDE + 16 * (lg ^ i);
 
   auto compute = [&](int j) {
     const char *kb = s_k[j & 1];
@@ -406,14 +409,10 @@ void prefill_kernel(PrefillLaunch p) {
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        // row d = 16 dt + lq of V^T, groups (8 ks2 + 4 half + lg) ^ ((d >> 3) & 11): the XOR
-        // splits into bits, so the address is a lane base (two variants, by dt's parity) plus
-        // an immediate -- no per-read address arithmetic -- and the high half is 32 bytes up
-        const char *vrow = vb + ((dt & 1) ? vt_lane_odd : vt_lane_even) + 16 * dt * V_STRIDE;
-        const int g_hi = 8 * (8 * (ks2 ^ ((dt >> 2) & 1)));
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + g_hi);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + g_hi + 32);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        // row d = 16 dt + lq of V^T, pair (4 ks2 + lg) ^ dt: a lane base (four variants, by
+        // dt & 3) plus an immediate
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(vb + vt_lane[dt & 3] + 16 * dt * V_STRIDE +
+                                                          64 * (ks2 ^ (dt >> 2)));
 #pragma unroll
         for (int qt2 = 0; qt2 < 2; ++qt2) o[dt][qt2] = mfma(a, pb[qt2][ks2], o[dt][qt2]);
       }
