@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--prewarm-ms", type=float, default=300.0,
                     help="before the warm-up steps, run steps back to back for this long so that the GPU's "
                          "clocks reach their sustained level (a short run otherwise times the clock ramp)")
+    ap.add_argument("--skip-probes", action="store_true",
+                    help="decode workloads: do not run the stream and gather bandwidth probes after the "
+                         "timed steps (for profiler counter passes)")
     ap.add_argument("--prefill-case", default="w5-rows",
                     help="--op prefill: w5-rows, chunk256-after8192 or prompt8192")
     ap.add_argument("--op", default="decode",
@@ -800,11 +803,12 @@ def main():
         "roofline": roofline,
         "input_generation_s": round(gen_s, 2),
     }
-    st = stream_ceiling(kv_bytes, prewarm_ms=min(100.0, args.prewarm_ms))
-    res["stream_read"] = st
-    res["pct_of_stream"] = round(100 * value / st["GBs"], 2)
-    res["kernel_pct_of_stream"] = round(100 * achieved / st["GBs"], 2)
-    if not mixed:
+    st = None if args.skip_probes else stream_ceiling(kv_bytes, prewarm_ms=min(100.0, args.prewarm_ms))
+    if st is not None:
+        res["stream_read"] = st
+        res["pct_of_stream"] = round(100 * value / st["GBs"], 2)
+        res["kernel_pct_of_stream"] = round(100 * achieved / st["GBs"], 2)
+    if not mixed and not args.skip_probes:
         gt = gather_ceiling(w, d, prewarm_ms=min(100.0, args.prewarm_ms))
         res["gather_read"] = gt
         res["pct_of_gather"] = round(100 * value / gt["GBs"], 2)
