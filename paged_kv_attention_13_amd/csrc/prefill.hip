@@ -243,8 +243,13 @@ void prefill_kernel(PrefillLaunch p) {
   const __bf16 *kpool = static_cast<const __bf16 *>(p.k_pool) + (size_t)g * page_elems;
   const __bf16 *vpool = static_cast<const __bf16 *>(p.v_pool) + (size_t)g * page_elems;
   const size_t phys_stride = (size_t)Hkv * page_elems;
+  // thread -> (token quad c_tq, 16-byte chunk c_dg).  The quad index is a bit permutation of
+  // tid >> 4 chosen so that the two 16-lane halves of each 32-lane half-wave take quads that
+  // differ in bit 2, i.e. fill opposite 8-byte halves of the V^T pairs below: their 8-byte
+  // stores then meet different banks instead of sharing one 16-byte slot
   const int c_dg = tid & 15;
-  const int c_tq = tid >> 4;                // 0..15
+  const int c_u = tid >> 4;                 // 4 * wave + (lane >> 4)
+  const int c_tq = ((c_u >> 3) << 3) | ((c_u & 1) << 2) | (((c_u >> 1) & 1) << 1) | ((c_u >> 2) & 1);
 
   // stage the block-table entries of every page the loads below can touch in LDS, so the
   // pipelined loads depend on one LDS read instead of a global load.  The loads cover
