@@ -692,7 +692,7 @@ def main():
             step()
         else:
             stages[0]()
-        if evs:
+        if evs and evs[1] is not None:
             evs[1].record()
         if two_stage:
             stages[1]()
@@ -717,7 +717,9 @@ def main():
     # 281 us bare, 286 us with an event pair around the decode kernel, 293 us with a third after
     # the merge), so the per-kernel events are recorded on every EVENT_STRIDE-th timed step only;
     # the step time is the wall clock over all timed steps.  With a scrub between steps the step
-    # time is the median of per-step events instead, so every step carries them.
+    # time is the median of per-step events instead, so every step carries a start and an end
+    # event, and only every other step the event between the two kernels (whose own cost would
+    # otherwise sit inside the measured step): the kernel time comes from those steps.
     if args.scrub_mib is None:
         args.scrub_mib = 1024 if accounting.workload_bytes(w)["kv"] < (1 << 30) else 0
     # the scrub reads (it does not write): a write would leave the caches full of dirty lines
@@ -727,6 +729,9 @@ def main():
     stride = 1 if scrub is not None else max(1, min(EVENT_STRIDE, args.steps // 8))
     sampled = list(range(0, args.steps, stride))
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    if scrub is not None and two_stage:
+        for i in sampled[1::2]:
+            evs[i][1] = None                 # step-time samples: no event between the kernels
     sampler = GpuSampler()
     torch.cuda.synchronize()
     sampler.start()
@@ -740,10 +745,12 @@ def main():
     gpu_state_summary = sampler.stop("the timed steps")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     last = 2 if two_stage else 1
+    split = [e for e in evs.values() if e[1] is not None]      # steps with the between-kernels event
     if scrub is not None:
-        ms_per_step = float(np.median([e[0].elapsed_time(e[last]) for e in evs.values()]))
-    k_ms = [e[0].elapsed_time(e[1]) for e in evs.values()]
-    m_ms = [e[1].elapsed_time(e[2]) for e in evs.values()] if two_stage else []
+        whole = [e for e in evs.values() if e[1] is None] or split
+        ms_per_step = float(np.median([e[0].elapsed_time(e[last]) for e in whole]))
+    k_ms = [e[0].elapsed_time(e[1]) for e in split]
+    m_ms = [e[1].elapsed_time(e[2]) for e in split] if two_stage else []
     kernel_ms = float(np.mean(k_ms))
 
     cb = accounting.workload_bytes(w)

@@ -30,7 +30,8 @@ constexpr int kCascadePrefixMinTiles = 2;   // shared-prefix calls, prefix part:
 constexpr int kVerifyTile = 32;          // verify kernel: tokens per tile
 constexpr int kVerifyMaxCols = 32;       // verify kernel: query columns (q_len x group) per kv head
 inline int verify_max_workers(int cus) { return cus * 4; }   // one verify wave per SIMD
-constexpr int kMqUnitCost = 4;           // multi-query kernel: start-up cost of a unit, in tiles
+constexpr int kMqUnitCost = 2;           // multi-query kernel: start-up cost of a unit, in tiles
+                                         // (FP8 rows of 128-8,192 tokens: 2 measured best of 0-4)
 constexpr int kDecodeUnitCost = 4;       // decode kernel: start-up cost of a unit, in 16-token
                                          // tiles (measured: each unit a wave starts delays its
                                          // end by ~4.5 us, the time of ~3.6 tiles)
