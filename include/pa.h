@@ -216,7 +216,12 @@ int pa_abi_version(void);
  * With num_workers == 0, rows bounded by max_seq_len <= 1024 tokens (and 64
  * pages) of an fp32 or bf16 cache, at most 2C (row, kv head) units, run one
  * workgroup per unit whose waves combine their results in LDS: workspace_bytes
- * is 0 and num_workers reports those waves.  Otherwise, with num_workers == 0
+ * is 0 and num_workers reports those waves.  When S = min(C / units,
+ * ceil(tiles / 4), 16) is at least 2 (tiles = ceil(max_seq_len / 16); at most C/2
+ * units of more than 4 tiles: a unit's one workgroup would leave CUs idle), each
+ * unit is instead cut over S workgroups; num_workers reports the S x units
+ * pieces and the workspace takes the layout below with S x units in place of
+ * the workers.  Otherwise, with num_workers == 0
  * the plan takes one worker wave per SIMD (4C), or two (8C) when no unit can
  * exceed 32 tiles or the cache is FP8, fewer for small work (at least 4 tiles
  * each, counting 4 start-up tiles per unit for fp32/bf16 caches); the
@@ -226,7 +231,7 @@ int pa_abi_version(void);
 pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
 
 /* Workspace bytes a pa_decode call with these arguments needs (the plan's
- * workspace_bytes; 0 on the one-workgroup-per-unit path and for an empty batch).
+ * workspace_bytes; 0 where whole units run one workgroup each and for an empty batch).
  * The caller allocates it (the library allocates nothing) and passes it in
  * a->workspace.  Returns SIZE_MAX, with pa_last_error() set, when the host-visible
  * arguments are invalid (the same checks as pa_decode_plan).  The workspace holds
@@ -302,12 +307,13 @@ pa_status pa_check_append_metadata(const pa_append_args *a_host);
  * decode row b's newest token: num_tokens == num_seqs, the two argument sets
  * describe the same pools, and slot_mapping[b] is -1 or the slot of position
  * seq_lens[b] - 1 of row b (pa_check_append_decode_metadata verifies this on
- * host copies).  When the decode plan runs one workgroup per (row, kv head)
+ * host copies).  When the decode plan runs workgroups per (row, kv head)
  * (rows within 1,024 tokens, at most 512 units, worker count left to the
- * library, fp32 or bf16 pools) this is one launch: each workgroup writes its row's new K/V to the
- * slot and takes position seq_len - 1 from the new rows rather than from the
- * slot, so no part of the launch reads memory it writes.  Otherwise the two
- * calls are queued one after the other.  For a decode loop whose layers each
+ * library, fp32 or bf16 pools) this is one launch (plus the merge when units are
+ * cut over several workgroups): a unit's first workgroup writes its row's new K/V
+ * to the slot and every workgroup takes position seq_len - 1 from the new rows
+ * rather than from the slot, so no part of the launch reads memory it writes.
+ * Otherwise the two calls are queued one after the other.  For a decode loop whose layers each
  * append one token and attend (one launch per layer instead of two). */
 pa_status pa_append_decode(const pa_append_args *app, const pa_decode_args *dec, void *stream);
 pa_status pa_check_append_decode_metadata(const pa_append_args *app_host, const pa_decode_args *dec_host);

@@ -544,13 +544,46 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch p) {
   const int g = h / G;
   const int hh = h % G;
   const int u = b * p.num_kv_heads + g;
-  int cnt = p.seg_count[u];
+  // units cut over workgroups have their pieces at fixed slots (no record to read)
+  const bool fixed = p.unit_mode && p.unit_pieces > 1;
+  int cnt = fixed ? p.unit_pieces : p.seg_count[u];
   if (cnt <= 1) return;                    // written directly by its only worker
   // slots u + w exist for the launch's workers w in [0, num_workers): a record that does
   // not come from the partials launch on this workspace gives wrong numbers, never a read
   // outside it
-  const int first = min(max(p.seg_first[u], 0), p.num_workers - 1);
+  const int first = fixed ? u * (cnt - 1) : min(max(p.seg_first[u], 0), p.num_workers - 1);
   cnt = min(cnt, p.num_workers - first);
+  float n0 = 0.f, n1 = 0.f, den = 0.f;
+  if (cnt <= 8) {
+    // every piece's (max, sum, two accumulators) in one round trip, then the same
+    // arithmetic in the same order as the general path below
+    float pm[8], pl[8];
+    float2 pa[8];
+    float M = kNegBig;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < cnt) {
+        const size_t slot = (size_t)(u + first + k) * G + hh;
+        pm[k] = p.part_m[slot];
+        pl[k] = p.part_l[slot];
+        pa[k] = *reinterpret_cast<const float2 *>(p.part_acc + slot * D + 2 * lane);
+        M = fmaxf(M, pm[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < cnt) {
+        const float wt = fast_exp2(pm[k] - M);
+        den = __builtin_fmaf(wt, pl[k], den);
+        n0 = __builtin_fmaf(wt, pa[k].x, n0);
+        n1 = __builtin_fmaf(wt, pa[k].y, n1);
+      }
+    }
+    const size_t o = ((size_t)b * p.num_q_heads + h) * D + 2 * lane;
+    store_out<OUT_BF16>(p.out, o, n0 / den);
+    store_out<OUT_BF16>(p.out, o + 1, n1 / den);
+    return;
+  }
   // the pieces' maxima, one per lane: one round trip however many pieces there are
   float M = kNegBig;
   for (int base = 0; base < cnt; base += 64)
@@ -558,7 +591,6 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeLaunch p) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   // then the pieces in order, eight at a time with all their loads issued before use
-  float n0 = 0.f, n1 = 0.f, den = 0.f;
   for (int base = 0; base < cnt; base += 8) {
     float pm[8], pl[8];
     float2 pa[8];
@@ -613,8 +645,11 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int Hq = p.num_q_heads;
   const int Hkv = p.num_kv_heads;
-  const int b = blockIdx.x / Hkv;
-  const int g = blockIdx.x % Hkv;
+  const int S = p.unit_pieces;                   // workgroups per unit
+  const int u = (int)blockIdx.x / S;
+  const int piece = (int)blockIdx.x % S;
+  const int b = u / Hkv;
+  const int g = u % Hkv;
   const int c = lane & 7;
   const int grp = lane >> 3;
 
@@ -648,9 +683,12 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
     vnew = static_cast<const char *>(p.v_new) + row_off;
   }
 
+  // this workgroup's share of the unit's tiles, then each wave's share of that
   const int nb = (L + TILE - 1) / TILE;
-  const int t_lo = wave * nb / NWU;
-  const int t_hi = (wave + 1) * nb / NWU;
+  const int pt0 = piece * nb / S;
+  const int pn = (piece + 1) * nb / S - pt0;
+  const int t_lo = pt0 + wave * pn / NWU;
+  const int t_hi = pt0 + (wave + 1) * pn / NWU;
   const int bs = p.block_size;
   const int log2bs = __builtin_ctz(bs);
   const size_t page_bytes = (size_t)bs * D * EB;
@@ -660,8 +698,9 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
   const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_bytes;
   const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_bytes;
   if constexpr (APPEND) {
-    // the appended row: 16 bytes per lane of wave 0
-    if (wave == 0 && new_slot >= 0 && lane < D * EB / 16) {
+    // the appended row: 16 bytes per lane of wave 0 of the unit's first workgroup (the
+    // workgroup whose tiles reach position L - 1 takes that token from the new rows)
+    if (piece == 0 && wave == 0 && new_slot >= 0 && lane < D * EB / 16) {
       const size_t dst = (size_t)(new_slot >> log2bs) * phys_stride + (size_t)g * page_bytes +
                          (size_t)(new_slot & (bs - 1)) * (D * EB) + 16 * lane;
       *reinterpret_cast<u32x4 *>(static_cast<char *>(p.k_pool_w) + dst) =
@@ -887,6 +926,9 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
     }
   }
   __syncthreads();
+  // a unit cut over several workgroups: its pieces take the fixed slots u * S + piece, which
+  // the merge kernel reads without piece records (a piece without tiles leaves max -1e30,
+  // sum 0)
   for (int i = threadIdx.x; i < G * D; i += NTU) {
     const int hh = i / D;
     const int d = i % D;
@@ -900,7 +942,16 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
       den = __builtin_fmaf(wt, s_ml[w][hh][1], den);
       num = __builtin_fmaf(wt, s_acc[w][hh][d], num);
     }
-    store_out<OUT_BF16>(p.out, ((size_t)b * Hq + g * G + hh) * D + d, num / den);
+    if (S > 1) {
+      const size_t slot = (size_t)(u * S + piece) * G + hh;
+      p.part_acc[slot * D + d] = num;
+      if (d == 0) {
+        p.part_m[slot] = M;
+        p.part_l[slot] = den;
+      }
+    } else {
+      store_out<OUT_BF16>(p.out, ((size_t)b * Hq + g * G + hh) * D + d, num / den);
+    }
   }
 }
 
@@ -908,7 +959,8 @@ template <int KV, int G>
 int launch_kv_g(const DecodeLaunch &L, hipStream_t st) {
   if (L.unit_mode) {
     if (L.kv_start) return (int)hipErrorInvalidValue;
-    dim3 ugrid((unsigned)L.num_seqs * L.num_kv_heads);
+    if (L.unit_pieces < 1 || (L.unit_pieces > 1 && !L.part_acc)) return (int)hipErrorInvalidValue;
+    dim3 ugrid((unsigned)L.num_seqs * L.num_kv_heads * (unsigned)L.unit_pieces);
     dim3 ublock(unit_waves(KV, G) * 64);
     if (L.k_new) {
       if (!L.v_new || !L.new_slots || !L.k_pool_w || !L.v_pool_w) return (int)hipErrorInvalidValue;
@@ -963,7 +1015,7 @@ int launch_decode_partials(const DecodeLaunch &L, void *stream) {
 }
 
 int launch_merge(const DecodeLaunch &L, void *stream) {
-  if (L.unit_mode) return 0;               // the unit kernel wrote every output itself
+  if (L.unit_mode && L.unit_pieces == 1) return 0;   // the unit kernel wrote every output itself
   hipStream_t st = static_cast<hipStream_t>(stream);
   dim3 grid(L.num_q_heads, L.num_seqs);
   if (L.out_dtype == PA_BF16)

@@ -91,13 +91,17 @@ pa_status pa_append_decode(const pa_append_args *app, const pa_decode_args *dec,
   s = prepare_decode(dec, &plan, &L);
   if (s != PA_OK) return s;
   if (L.unit_mode) {
-    // one launch: each unit's workgroup appends its row's new token and attends over it
+    // one launch (plus the merge when units are cut over several workgroups): the unit's
+    // first workgroup appends its row's new token, and every workgroup takes position
+    // seq_len - 1 from the new rows, so the results are those of pa_append + pa_decode
     L.k_new = app->k;
     L.v_new = app->v;
     L.new_slots = app->slot_mapping;
     L.k_pool_w = app->k_pool;
     L.v_pool_w = app->v_pool;
-    return hip_status(launch_decode_partials(L, stream), "append + decode");
+    s = hip_status(launch_decode_partials(L, stream), "append + decode");
+    if (s != PA_OK) return s;
+    return hip_status(launch_merge(L, stream), "merge");
   }
   s = pa_append(app, stream);
   if (s != PA_OK) return s;

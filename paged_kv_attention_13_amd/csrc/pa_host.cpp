@@ -133,7 +133,16 @@ pa_status plan_decode(const pa_decode_args *a, pa_plan *plan) {
   }
   plan->num_workers = nw;
   plan->tile_tokens = tile;
-  if (decode_unit_mode(a, cus)) {
+  if (decode_unit_mode(a, cus) && decode_unit_pieces(a, cus) > 1) {
+    // few units: each cut over S workgroups (num_workers reports the S x units pieces),
+    // whose partials take the split layout below with S x units slots past the units
+    const size_t units = (size_t)a->num_seqs * a->num_kv_heads;
+    const int S = decode_unit_pieces(a, cus);
+    plan->num_workers = (int32_t)(units * S);
+    const size_t slots = (units + units * S) * (size_t)(a->num_q_heads / a->num_kv_heads);
+    plan->workspace_bytes = round_up(2 * units * sizeof(int32_t), 256) + 2 * round_up(slots * sizeof(float), 256) +
+                            round_up(slots * kHeadDim * sizeof(float), 256);
+  } else if (decode_unit_mode(a, cus)) {
     // one workgroup of 8 (or 4) waves per (row, kv head) unit, merged in LDS
     const int waves = unit_waves(a->kv_dtype, a->num_q_heads / a->num_kv_heads);
     plan->num_workers = (int32_t)std::min<int64_t>((int64_t)a->num_seqs * a->num_kv_heads * waves, INT32_MAX);
@@ -172,7 +181,8 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   L->out_dtype = a->out_dtype;
   L->scale = a->scale;
   L->unit_mode = decode_unit_mode(a, device_cus());
-  if (a->num_seqs > 0 && !L->unit_mode) {
+  L->unit_pieces = L->unit_mode ? decode_unit_pieces(a, device_cus()) : 1;
+  if (a->num_seqs > 0 && (!L->unit_mode || L->unit_pieces > 1)) {
     if (!a->workspace || a->workspace_bytes < plan.workspace_bytes)
       return set_error(PA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, plan needs %zu",
                        a->workspace ? a->workspace_bytes : (size_t)0, plan.workspace_bytes);

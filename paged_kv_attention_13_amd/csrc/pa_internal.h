@@ -84,7 +84,10 @@ struct DecodeLaunch {
   int kv_dtype;
   int out_dtype;
   float scale;
-  int unit_mode;       // 1: one workgroup per (row, kv head) unit, no workspace, no merge
+  int unit_mode;       // 1: one workgroup per (row, kv head) unit, merged in LDS
+  int unit_pieces;     // unit mode: workgroups per unit; 1 = no workspace, no merge, else each
+                       // writes the partial of its share of the unit's tiles to slot
+                       // unit * unit_pieces + piece and the merge kernel combines them
   // fused append (unit mode only): row b's new token k_new/v_new[b] ([B][Hkv][D], the pool
   // dtype) is written to slot new_slots[b] (-1: none) of the pools, and used for position
   // seq_len - 1 instead of reading that slot
@@ -243,6 +246,19 @@ inline bool decode_unit_mode(const pa_decode_args *a, int cus) {
   return a->num_workers == 0 && a->num_seqs > 0 && a->kv_dtype != PA_FP8_E4M3 &&
          a->max_seq_len <= kUnitMaxTokens && a->max_seq_len <= 64 * a->block_size &&
          (int64_t)a->num_seqs * a->num_kv_heads <= unit_max_units(cus);
+}
+// Unit mode with few units: each unit's tiles are cut over this many workgroups, so that
+// more CUs than units stream the cache (a unit's workgroup alone is bound by what one CU
+// keeps in flight); at most one per CU in all, at least kUnitPieceTiles tiles each.
+constexpr int kUnitPieceTiles = 4;
+constexpr int kUnitMaxPieces = 16;
+inline int decode_unit_pieces(const pa_decode_args *a, int cus) {
+  const int64_t units = (int64_t)a->num_seqs * a->num_kv_heads;
+  const int64_t tiles = (a->max_seq_len + 15) / 16;        // decode tiles (fp32 and bf16 pools)
+  int64_t s = units > 0 ? cus / units : 1;
+  if (s > (tiles + kUnitPieceTiles - 1) / kUnitPieceTiles) s = (tiles + kUnitPieceTiles - 1) / kUnitPieceTiles;
+  if (s > kUnitMaxPieces) s = kUnitMaxPieces;
+  return s >= 2 ? (int)s : 1;
 }
 // Resident multi-query waves: one per SIMD, two for FP8 pools with <= 16 columns.
 inline int mq_max_workers(int kv_dtype, int slot_cols, int cus) {

@@ -162,10 +162,22 @@ def test_plan_choices(b):
     # short units between one and two waves per SIMD round up to two
     a = _args(b, num_seqs=130, max_seq_len=64, max_blocks_per_seq=4)   # 1,040 units x 8 tiles
     assert b.plan(a).num_workers == 2048
-    # rows within 1,024 tokens: one workgroup of 8 waves per (row, kv head), no workspace
+    # rows within 1,024 tokens: one workgroup of 8 waves per (row, kv head), no workspace ...
+    a = _args(b, num_seqs=40, max_seq_len=1024, max_blocks_per_seq=64)
+    p = b.plan(a)
+    assert p.num_workers == 40 * 8 * 8 and p.workspace_bytes == 0
+    # ... or, with fewer units than CUs, each unit cut over S = min(CUs / units, tiles / 4, 16)
+    # workgroups (24 units: S = 10), whose partials take the split layout with S x units slots
     a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
     p = b.plan(a)
-    assert p.num_workers == 3 * 8 * 8 and p.workspace_bytes == 0
+    units, S = 3 * 8, 10
+    slots = (units + units * S) * 4
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert p.num_workers == units * S
+    assert p.workspace_bytes == r256(2 * units * 4) + 2 * r256(slots * 4) + r256(slots * 512)
+    a = _args(b, num_seqs=1, max_seq_len=48, max_blocks_per_seq=4)      # 3 tiles: one piece per unit
+    assert b.plan(a).workspace_bytes == 0
+    a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
     a.num_workers = 5                                         # an explicit count keeps the split
     assert b.plan(a).num_workers == 5 and b.plan(a).workspace_bytes > 0
     a.num_workers = 0
@@ -566,14 +578,15 @@ def test_decode_workspace_size_is_the_plans(b):
     needed) and SIZE_MAX, with the reason in pa_last_error, for invalid arguments."""
     shapes = [dict(num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192),
               dict(num_seqs=32, max_blocks_per_seq=256, max_seq_len=4096),
-              dict(num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64),          # one workgroup per unit
+              dict(num_seqs=40, max_seq_len=1024, max_blocks_per_seq=64),         # one workgroup per unit
+              dict(num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64),          # units cut over workgroups
               dict(num_seqs=55, block_size=64, max_blocks_per_seq=128, max_seq_len=8192, num_workers=7),
               dict(num_seqs=0)]
     for kw in shapes:
         a = _args(b, **kw)
         n = b.LIB.pa_decode_workspace_size(ctypes.byref(a))
         assert n == b.plan(a).workspace_bytes, kw
-    a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
+    a = _args(b, num_seqs=40, max_seq_len=1024, max_blocks_per_seq=64)
     assert b.LIB.pa_decode_workspace_size(ctypes.byref(a)) == 0
     a = _args(b, kv_dtype=2, k_scale=0x10000, v_scale=0x10000, num_seqs=128, max_seq_len=8192,
               max_blocks_per_seq=512)

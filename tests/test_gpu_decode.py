@@ -200,19 +200,29 @@ def test_split_invariance():
         assert np.max(np.abs(o - outs[0])) <= 8e-3
 
 
+@pytest.mark.parametrize("rows", ["few", "many"])
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (64, 8)])
-def test_short_rows_one_workgroup_per_unit(hq, hkv):
+def test_short_rows_one_workgroup_per_unit(hq, hkv, rows):
     """Rows within 1,024 tokens with the worker count left to the library run one workgroup
-    per (row, kv head), its waves merged in LDS (no workspace); they match the oracle and
-    the balanced split of the same rows."""
-    _announce(f"one workgroup per unit, hq={hq} hkv={hkv}")
+    per (row, kv head), its waves merged in LDS; with fewer units than CUs ("few": 72 units,
+    each cut over 3 workgroups whose partials the merge kernel combines), else whole units
+    and no workspace ("many": 360 units).  Both match the oracle and the balanced split of
+    the same rows."""
+    _announce(f"one workgroup per unit, hq={hq} hkv={hkv} rows={rows}")
     from paged_kv_attention_13_amd import binding
-    w = _small([1, 15, 16, 17, 48, 63, 300, 1000, 1024], hq=hq, hkv=hkv, seed=60 + hq)
+    lens = [1, 15, 16, 17, 48, 63, 300, 1000, 1024]
+    if rows == "many":
+        lens = lens * 5
+    w = _small(lens, hq=hq, hkv=hkv, seed=60 + hq + len(lens))
     a = binding.DecodeArgs()
     a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = w.num_seqs, hq, hkv, 128
     a.block_size, a.num_blocks, a.max_blocks_per_seq = w.block_size, w.num_blocks, w.max_blocks_per_seq
     a.max_seq_len, a.q_dtype, a.kv_dtype, a.out_dtype = w.max_seq_len, 1, 1, 1
-    assert binding.plan(a).workspace_bytes == 0
+    pl = binding.plan(a)
+    if rows == "many":
+        assert pl.workspace_bytes == 0
+    else:
+        assert pl.workspace_bytes > 0 and pl.num_workers == w.num_seqs * hkv * 3
     ref = oracle.paged_attention_workload(w)
     unit = run_decode(w, out_dtype="f32")
     split = run_decode(w, out_dtype="f32", num_workers=37)

@@ -57,20 +57,31 @@ def test_noalloc_equals_pa_decode_on_two_calls(kv_fmt):
 
 
 @pytest.mark.gpu
-def test_noalloc_short_rows_need_no_scratch():
-    """Rows on the one-workgroup-per-unit path use no partials at all."""
-    _announce("noalloc short rows")
+@pytest.mark.parametrize("rows", ["whole", "pieces"])
+def test_noalloc_short_rows(rows):
+    """Rows on the one-workgroup-per-unit path: with whole units (45 rows, 360 units) no
+    partials at all; with few units (3 rows, 24 units, each cut over 10 workgroups) the
+    pieces' partials go to the static scratch.  Both equal pa_decode bit for bit."""
+    _announce(f"noalloc short rows, {rows}")
     import torch
     from paged_kv_attention_13_amd import binding as b
     from paged_kv_attention_13_amd.device import to_device
-    w = pa_inputs.make_workload(name="noalloc", seq_lens=[1, 40, 1000], block_size=16, seed=5, extra_blocks=2,
+    lens = [1, 40, 1000] * (15 if rows == "whole" else 1)
+    w = pa_inputs.make_workload(name="noalloc", seq_lens=lens, block_size=16, seed=5, extra_blocks=2,
                                 poison_unused=True)
     d = to_device(w)
-    out = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
-    a = _args(b, w, d, out)
-    assert b.decode_workspace_bytes(a) == 0
-    b.decode_noalloc_args_call(a)
+    ref_out = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    a = _args(b, w, d, ref_out)
+    nbytes = b.decode_workspace_bytes(a)
+    assert (nbytes == 0) == (rows == "whole")
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    b.decode_args_call(a)
+    out = torch.full(d["q"].shape, float("nan"), dtype=torch.float32, device="cuda")
+    n = _args(b, w, d, out)
+    b.decode_noalloc_args_call(n)
     torch.cuda.synchronize()
+    assert torch.equal(out, ref_out)
     compare(out.cpu().numpy().astype(np.float64), oracle.paged_attention_workload(w), 5e-3, what="noalloc short")
 
 
