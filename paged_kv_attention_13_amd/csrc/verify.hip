@@ -636,6 +636,33 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   // outside it
   const int first = min(max(p.seg_first[u], 0), p.num_workers - 1);
   cnt = min(cnt, p.num_workers - first);
+  float n0 = 0.f, n1 = 0.f, den = 0.f;
+  if (cnt <= 8) {
+    // every piece's (max, sum, two accumulators) in one round trip, then the same
+    // arithmetic in the same order as the general path below
+    float pm[8], pl[8];
+    float2 pa[8];
+    float M = kNegBig;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < cnt) {
+        const size_t slot = (size_t)(u + first + k) * p.slot_cols + c;
+        pm[k] = p.part_m[slot];
+        pl[k] = p.part_l[slot];
+        pa[k] = *reinterpret_cast<const float2 *>(p.part_acc + slot * D + 2 * lane);
+        M = fmaxf(M, pm[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < cnt) {
+        const float wt = fast_exp2(pm[k] - M);
+        den = __builtin_fmaf(wt, pl[k], den);
+        n0 = __builtin_fmaf(wt, pa[k].x, n0);
+        n1 = __builtin_fmaf(wt, pa[k].y, n1);
+      }
+    }
+  } else {
   // the pieces' maxima, one per lane: one round trip however many pieces there are
   float M = kNegBig;
   for (int base = 0; base < cnt; base += 64)
@@ -643,7 +670,6 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   // then the pieces in order, eight at a time with all their loads issued before use
-  float n0 = 0.f, n1 = 0.f, den = 0.f;
   for (int base = 0; base < cnt; base += 8) {
     float pm[8], pl[8];
     float2 pa[8];
@@ -665,6 +691,7 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
         n1 = __builtin_fmaf(wt, pa[k].y, n1);
       }
     }
+  }
   }
   const size_t o = ((size_t)(qbase + c / G) * p.num_q_heads + g * G + c % G) * D + 2 * lane;
   if constexpr (OUT_BF16) {
