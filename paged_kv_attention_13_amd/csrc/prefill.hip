@@ -193,6 +193,10 @@ void prefill_kernel(PrefillLaunch p) {
   const int row = p.first_row + row_local;
   const int q_begin = p.q_start_loc[row];
   const int n = p.q_start_loc[row + 1] - q_begin;
+  // a split launch's piece length: its loads go out beside the row's metadata, before any
+  // exit, so that the two share one round trip (chunk of 256 after 8,192: 66.5 -> 64.9 us)
+  const int C = p.splits > 1 ? __builtin_amdgcn_readfirstlane(piece_tiles<QB>(p, threadIdx.x & 63, Hkv * hblocks))
+                             : 1 << 30;
   if (qt * QB >= n) return;                // whole workgroup: past this row's chunk
   const int L = p.seq_lens[row];
   const int prior = L - n;
@@ -208,7 +212,6 @@ void prefill_kernel(PrefillLaunch p) {
   const int kv_end = prior + blk_last_q + 1;              // tokens the unit visits
   const int ntile = (kv_end + KT - 1) / KT;
   // this workgroup's piece of the unit: tiles [j_begin, j_end)
-  const int C = __builtin_amdgcn_readfirstlane(piece_tiles<QB>(p, tid & 63, Hkv * hblocks));
   const int j_begin = piece * C;
   if (j_begin >= ntile) return;            // whole workgroup: the unit has fewer pieces
   const int j_end = min(ntile, j_begin + C);
@@ -507,14 +510,15 @@ __global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
   const int g = blockIdx.y / hblocks;
   const int hb = blockIdx.y % hblocks;
   const int row = p.first_row + blockIdx.z;
+  // metadata and piece length in one round trip (their loads issued before any exit)
   const int q_begin = p.q_start_loc[row];
   const int n = p.q_start_loc[row + 1] - q_begin;
-  if (qt * QB >= n) return;
   const int L = p.seq_lens[row];
-  const int prior = L - n;
-  const int ntile = (prior + min(qt * QB + QB, n) + KT - 1) / KT;
   const int tid = threadIdx.x;
   const int C = __builtin_amdgcn_readfirstlane(piece_tiles<QB>(p, tid & 63, Hkv * hblocks));
+  if (qt * QB >= n) return;
+  const int prior = L - n;
+  const int ntile = (prior + min(qt * QB + QB, n) + KT - 1) / KT;
   if (ntile <= C) return;                  // the prefill kernel stored this unit itself
   const int npieces = (ntile + C - 1) / C;
   const int lane = tid & 63;
@@ -530,6 +534,19 @@ __global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
   const float *__restrict__ pml = p.part_ml + slot0 * (QW * 2);
   constexpr size_t kPieceO = (size_t)NWP * QW * D;       // floats between pieces of one slot
   constexpr size_t kPieceML = (size_t)NWP * QW * 2;
+  // every load of the merge (the pieces' outputs and their (max, sum) pairs) is issued
+  // before any use: one round trip
+  const int half = lane >> 5;
+  const int d = 4 * (lane & 31);
+  f32x4 pv[QM / 2][kPrefillMaxSplits];
+#pragma unroll
+  for (int qq = 0; qq < QM; qq += 2) {
+    const int ql = qm0 + qq + half;
+#pragma unroll
+    for (int s = 0; s < kPrefillMaxSplits; ++s)
+      pv[qq / 2][s] = (s < npieces && ql < q_lim) ? *reinterpret_cast<const f32x4 *>(po + s * kPieceO + ql * D + d)
+                                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float wt[kPrefillMaxSplits];
   {
     const int c = qm0 + (lane & (QM - 1));
@@ -555,8 +572,6 @@ __global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
 #pragma unroll
     for (int s = 0; s < kPrefillMaxSplits; ++s) wt[s] = c < q_lim ? wt[s] / den : 0.f;
   }
-  const int half = lane >> 5;
-  const int d = 4 * (lane & 31);
 #pragma unroll
   for (int qq = 0; qq < QM; qq += 2) {
     const int ql = qm0 + qq + half;
@@ -564,8 +579,7 @@ __global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
 #pragma unroll
     for (int s = 0; s < kPrefillMaxSplits; ++s) {
       const float w = __shfl(wt[s], qq + half);
-      if (s < npieces && ql < q_lim)
-        acc += w * *reinterpret_cast<const f32x4 *>(po + s * kPieceO + ql * D + d);
+      if (s < npieces && ql < q_lim) acc += w * pv[qq / 2][s];
     }
     if (ql < q_lim) store4<OUT_BF16>(p.out, ((size_t)(q_begin + q0 + ql) * Hq + h) * D + d, acc);
   }
