@@ -15,7 +15,9 @@
 // Work decomposition.  Short rows (bounded by 1,024 tokens, worker count left
 // to the library) run decode_unit_kernel: one workgroup per (row, kv head),
 // its waves merged in LDS, no workspace and no merge launch (and, for
-// pa_append_decode, the row's new token appended in the same launch).
+// pa_append_decode, the row's new token appended in the same launch); with
+// fewer units than CUs each unit is cut over several workgroups instead, whose
+// partials sit in fixed slots for the merge kernel.
 // Otherwise the work is the flattened sequence of (row, kv head, 16-token
 // tile) units, each unit preceded by a few virtual tiles that stand for its
 // start-up cost, cut into equal contiguous ranges, one per worker wave; the
