@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 /* Element types.  Supported (q, kv, out) combinations:
  *   (F32, F32, F32|BF16), (BF16, BF16, BF16|F32), (BF16, FP8_E4M3, BF16|F32). */
@@ -264,6 +264,27 @@ pa_status pa_decode(const pa_decode_args *a, void *stream);
  * threads) race and must be serialised by the caller.  No memory is allocated and
  * nothing is synchronised; the array's device address is looked up once per device. */
 pa_status pa_decode_noalloc(const pa_decode_args *a, void *stream);
+
+/* Debug builds of the library, compiled with PA_DEVICE_CHECKS=1 (libpa_kv_checked.so,
+ * `python -m paged_kv_attention_13_amd.build --checked`), check the device-resident
+ * metadata that the calls above take as a precondition, at each use: a block id read from
+ * the block table outside [0, num_blocks) (the table lists which pool blocks hold a request's
+ * tokens, in order: "How does TensorRT-LLM work", outcomeschool.com, section "The paged KV
+ * cache"), a row length outside [1, min(max_seq_len, max_blocks_per_seq * block_size)], a
+ * row's query count outside [1, its length], an append slot outside the pool.  The kernel
+ * then ors a bit below into a per-GPU flags word and continues with a safe value (block 0,
+ * the clamped length or count, the token skipped), so the call never reads or writes outside
+ * its buffers; its results are then meaningless.  Other builds compile the checks out. */
+#define PA_CHECK_BLOCK_ID 1u
+#define PA_CHECK_SEQ_LEN 2u
+#define PA_CHECK_Q_LEN 4u
+#define PA_CHECK_SLOT 8u
+/* 1 in a build with the device checks, else 0. */
+int pa_device_checks(void);
+/* Synchronises the current device, stores the or of the PA_CHECK_* bits recorded since the
+ * last call in *flags (always 0 in other builds) and clears the word.  For tests and
+ * debugging: it waits for all work on the device. */
+pa_status pa_device_check_flags(uint32_t *flags);
 
 /* The two stages of pa_decode, callable separately (e.g. to time one).  On the
  * one-workgroup-per-unit plan pa_decode_partials writes every output and

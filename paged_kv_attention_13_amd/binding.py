@@ -28,7 +28,7 @@ EXPORTED = ["pa_abi_version", "pa_decode_plan", "pa_mixed_workspace_size", "pa_d
             "pa_decode_cascade", "pa_check_cascade_metadata", "pa_append_decode",
             "pa_check_append_decode_metadata", "pa_status_string", "pa_last_error",
             "pa_decode_workspace_size", "pa_check_metadata", "pa_stream_read", "pa_decode_noalloc",
-            "pa_gather_read"]
+            "pa_gather_read", "pa_device_checks", "pa_device_check_flags"]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -142,6 +142,8 @@ def _load():
         "pa_check_cascade_metadata": ([P(CascadeArgs)], ctypes.c_int),
         "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "pa_last_error": ([], ctypes.c_char_p),
+        "pa_device_checks": ([], ctypes.c_int),
+        "pa_device_check_flags": ([P(ctypes.c_uint32)], ctypes.c_int),
     }
     for name, (argtypes, restype) in sigs.items():
         fn = getattr(lib, name)
@@ -156,6 +158,17 @@ LIB = _load()
 def check(status: int) -> None:
     if status != 0:
         raise PagedAttentionError(status, LIB.pa_last_error().decode())
+
+
+CHECK_BLOCK_ID, CHECK_SEQ_LEN, CHECK_Q_LEN, CHECK_SLOT = 1, 2, 4, 8
+
+
+def device_check_flags() -> int:
+    """``pa_device_check_flags``: synchronise the device and return (and clear) the PA_CHECK_*
+    bits the kernels of a debug build (``pa_device_checks() == 1``) recorded; 0 otherwise."""
+    v = ctypes.c_uint32(0)
+    check(LIB.pa_device_check_flags(ctypes.byref(v)))
+    return int(v.value)
 
 
 # ---------------------------------------------------------------------------

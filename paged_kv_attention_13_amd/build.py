@@ -34,12 +34,17 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    out = os.path.join(PKG, LIB_NAME)
+CHECKED_LIB_NAME = "libpa_kv_checked.so"
+
+
+def build(verbose: bool = False, checked: bool = False) -> str:
+    """Build the library; with ``checked``, the debug build whose kernels check the device
+    metadata at each use (PA_DEVICE_CHECKS=1), as ``libpa_kv_checked.so``."""
+    out = os.path.join(PKG, CHECKED_LIB_NAME if checked else LIB_NAME)
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS,
-           *sources(), "-o", tmp]
+           *(["-DPA_DEVICE_CHECKS=1"] if checked else []), *sources(), "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -76,4 +81,4 @@ def build_host_only(out_dir: str = None, sanitize: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, checked="--checked" in sys.argv))

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "checks.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendLaunch p) {
   const size_t th = i >> 4;
   const int g = (int)(th % p.num_kv_heads);
   const int t = (int)(th / p.num_kv_heads);
-  const int slot = p.slot_mapping[t];
+  const int slot = checked_slot(p.slot_mapping[t], p.num_blocks, p.block_size, p.check_flags);
   if (slot < 0) return;
   const int log2bs = __builtin_ctz(p.block_size);
   const int blk = slot >> log2bs;

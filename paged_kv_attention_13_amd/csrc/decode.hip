@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "checks.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
   // tokens of row r this kernel covers
   auto span_of = [&](int r) -> int {
     if constexpr (CASCADE) return p.seq_lens[r] - p.kv_start[r];
-    else return p.seq_lens[r];
+    else return checked_len(p.seq_lens[r], p.max_len, p.check_flags);
   };
 
   // Each unit counts unit_cost extra virtual tiles ahead of its real ones: starting a
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeLaunch p) {
       for (int r = 0; r < TPL; ++r) {
         const int tok0 = tok_begin + t * TILE + 8 * r;
         const int page = min(tok0 >> log2bs, last_page);
-        const int phys = __builtin_amdgcn_readlane(tbl, page - chunk_base);
+        const int phys = checked_block(__builtin_amdgcn_readlane(tbl, page - chunk_base), p.num_blocks, p.check_flags);
         // scalar page base + 32-bit per-lane offset (global_load ... saddr form); the
         // cache is streamed once per step, so the loads are non-temporal (measured
         // ~10% more HBM bandwidth than cached loads on MI355X)
@@ -656,7 +657,7 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
   const int grp = lane >> 3;
 
   // independent loads first
-  const int L = p.seq_lens[b];
+  const int L = checked_len(p.seq_lens[b], p.max_len, p.check_flags);
   const int tbl = p.block_table[(size_t)b * p.max_blocks_per_seq + min(lane, p.max_blocks_per_seq - 1)];
   uint32_t qb[G][8];
   float qf[G][16];
@@ -679,7 +680,7 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
   const char *knew = nullptr;
   const char *vnew = nullptr;
   if constexpr (APPEND) {
-    new_slot = p.new_slots[b];
+    new_slot = checked_slot(p.new_slots[b], p.num_blocks, p.block_size, p.check_flags);
     const size_t row_off = ((size_t)b * Hkv + g) * D * EB;
     knew = static_cast<const char *>(p.k_new) + row_off;
     vnew = static_cast<const char *>(p.v_new) + row_off;
@@ -731,7 +732,7 @@ __global__ __launch_bounds__(unit_waves(KV, G) * 64) void decode_unit_kernel(Dec
       for (int r = 0; r < TPL; ++r) {
         const int tok0 = tok_begin + t * TILE + 8 * r;
         const int page = min(tok0 >> log2bs, last_page);
-        const int phys = __builtin_amdgcn_readlane(tbl, page);
+        const int phys = checked_block(__builtin_amdgcn_readlane(tbl, page), p.num_blocks, p.check_flags);
         const char *kp = kpool + (size_t)phys * phys_stride;
         const char *vp = vpool + (size_t)phys * phys_stride;
         const uint32_t off = (uint32_t)(((tok0 + grp) & (bs - 1)) * (D * EB) + lane_off);

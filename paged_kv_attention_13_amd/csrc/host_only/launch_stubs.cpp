@@ -22,6 +22,11 @@ int launch_gather_read(const void *, const int64_t *, long long, int, uint32_t *
 int fork_side_stream(void *, void **) { return kNoDevice; }
 int static_scratch(void **) { return kNoDevice; }
 int join_side_stream(void *) { return kNoDevice; }
+unsigned int *device_check_flags() { return nullptr; }
+int read_and_clear_check_flags(uint32_t *flags) {
+  *flags = 0;
+  return PA_DEVICE_CHECKS ? kNoDevice : 0;
+}
 const char *hip_error_name(int) { return "hipErrorNoDevice (host-only build)"; }
 
 }  // namespace pa

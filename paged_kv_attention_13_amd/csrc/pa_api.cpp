@@ -37,6 +37,13 @@ pa_status pa_decode_partials(const pa_decode_args *a, void *stream) {
   return hip_status(launch_decode_partials(L, stream), "decode");
 }
 
+int pa_device_checks(void) { return PA_DEVICE_CHECKS; }
+
+pa_status pa_device_check_flags(uint32_t *flags) {
+  if (!flags) return set_error(PA_ERR_NULL_POINTER, "flags is NULL");
+  return hip_status(read_and_clear_check_flags(flags), "device check flags");
+}
+
 pa_status pa_decode_noalloc(const pa_decode_args *a, void *stream) {
   if (!a) return set_error(PA_ERR_NULL_POINTER, "argument struct is NULL");
   pa_decode_args b = *a;
@@ -124,6 +131,8 @@ pa_status pa_append(const pa_append_args *a, void *stream) {
   L.block_size = a->block_size;
   L.src_dtype = a->src_dtype;
   L.kv_dtype = a->kv_dtype;
+  L.num_blocks = a->num_blocks;
+  L.check_flags = device_check_flags();
   return hip_status(launch_append(L, stream), "append");
 }
 
@@ -189,6 +198,10 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.num_kv_heads = b.num_kv_heads;
     P.block_size = b.block_size;
     P.max_blocks_per_seq = b.max_blocks_per_seq;
+    P.num_blocks = b.num_blocks;
+    P.max_len = max_len_of(&b);
+    P.total_q = a->total_q;
+    P.check_flags = device_check_flags();
     P.max_q_len = a->max_q_len;
     P.out_dtype = b.out_dtype;
     P.scale = b.scale;

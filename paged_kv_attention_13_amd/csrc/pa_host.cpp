@@ -23,6 +23,11 @@ bool is_pow2_block(int bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 12
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
+// the longest row a call's metadata allows (the checked builds' bound on seq_lens)
+int max_len_of(const pa_decode_args *a) {
+  return (int)std::min<int64_t>(a->max_seq_len, (int64_t)a->max_blocks_per_seq * a->block_size);
+}
+
 pa_status set_error(pa_status s, const char *fmt, ...) {
   char buf[512];
   va_list ap;
@@ -173,6 +178,10 @@ pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, Decod
   L->num_kv_heads = a->num_kv_heads;
   L->block_size = a->block_size;
   L->max_blocks_per_seq = a->max_blocks_per_seq;
+  L->num_blocks = a->num_blocks;
+  L->max_len = max_len_of(a);
+  L->total_q = a->num_seqs;
+  L->check_flags = device_check_flags();
   L->num_workers = plan.num_workers;
   L->workers_auto = a->num_workers == 0;
   L->min_tiles = kMinTilesPerWorker;
@@ -319,6 +328,10 @@ pa_status make_verify_launch(const pa_mixed_args *a, int workers, size_t verify_
   V->num_kv_heads = b.num_kv_heads;
   V->block_size = b.block_size;
   V->max_blocks_per_seq = b.max_blocks_per_seq;
+  V->num_blocks = b.num_blocks;
+  V->max_len = max_len_of(&b);
+  V->total_q = a->total_q;
+  V->check_flags = device_check_flags();
   V->num_workers = workers;
   V->workers_auto = b.num_workers == 0;
   V->min_tiles = kMinTilesPerWorker;
@@ -410,6 +423,10 @@ pa_status plan_cascade(const pa_cascade_args *a, bool need_device_pointers, Deco
   pre->num_kv_heads = b.num_kv_heads;
   pre->block_size = b.block_size;
   pre->max_blocks_per_seq = b.max_blocks_per_seq;
+  pre->num_blocks = b.num_blocks;
+  pre->max_len = max_len_of(&b);
+  pre->total_q = b.num_seqs;
+  pre->check_flags = device_check_flags();
   pre->num_workers = pw;
   pre->workers_auto = b.num_workers == 0;
   pre->min_tiles = kCascadePrefixMinTiles;
@@ -479,6 +496,10 @@ pa_status make_decode_mq_launch(const pa_decode_args *a, const pa_plan &plan, Ve
   V->num_kv_heads = a->num_kv_heads;
   V->block_size = a->block_size;
   V->max_blocks_per_seq = a->max_blocks_per_seq;
+  V->num_blocks = a->num_blocks;
+  V->max_len = max_len_of(a);
+  V->total_q = a->num_seqs;
+  V->check_flags = device_check_flags();
   V->num_workers = plan.num_workers;
   V->workers_auto = a->num_workers == 0;
   V->min_tiles = kMinTilesPerWorker;

@@ -76,6 +76,12 @@ struct DecodeLaunch {
   int num_kv_heads;
   int block_size;
   int max_blocks_per_seq;
+  // debug builds (PA_DEVICE_CHECKS=1): the metadata bounds the kernels check at each use,
+  // and the device word their violations are or-ed into (null in other builds)
+  int num_blocks;
+  int max_len;                   // min(max_seq_len, max_blocks_per_seq * block_size)
+  int total_q;                   // rows of q and out
+  unsigned int *check_flags;
   int num_workers;
   int workers_auto;    // 1 when the library chose num_workers (the kernel may use fewer)
   int min_tiles;       // with workers_auto: at least this many tiles per worker (the plan
@@ -112,6 +118,12 @@ struct PrefillLaunch {
   int num_kv_heads;
   int block_size;
   int max_blocks_per_seq;
+  // debug builds (PA_DEVICE_CHECKS=1): the metadata bounds the kernels check at each use,
+  // and the device word their violations are or-ed into (null in other builds)
+  int num_blocks;
+  int max_len;                   // min(max_seq_len, max_blocks_per_seq * block_size)
+  int total_q;                   // rows of q and out
+  unsigned int *check_flags;
   int max_q_len;
   int out_dtype;
   float scale;
@@ -153,6 +165,12 @@ struct VerifyLaunch {
   int num_kv_heads;
   int block_size;
   int max_blocks_per_seq;
+  // debug builds (PA_DEVICE_CHECKS=1): the metadata bounds the kernels check at each use,
+  // and the device word their violations are or-ed into (null in other builds)
+  int num_blocks;
+  int max_len;                   // min(max_seq_len, max_blocks_per_seq * block_size)
+  int total_q;                   // rows of q and out
+  unsigned int *check_flags;
   int num_workers;
   int workers_auto;              // 1 when the library chose num_workers (the kernel may use fewer)
   int min_tiles;                 // with workers_auto: at least this many tiles per worker
@@ -203,10 +221,26 @@ struct AppendLaunch {
   int block_size;
   int src_dtype;
   int kv_dtype;
+  int num_blocks;                // debug builds: slots must lie below num_blocks * block_size
+  unsigned int *check_flags;     // debug builds: violations or-ed here (else null)
 };
+
+// Debug builds compiled with PA_DEVICE_CHECKS=1 check the device-resident metadata at each
+// use (block ids, row lengths, query counts, append slots) and record violations in a per-device
+// flags word instead of reading or writing out of bounds; other builds compile the checks out.
+#ifndef PA_DEVICE_CHECKS
+#define PA_DEVICE_CHECKS 0
+#endif
+// The flags word of the current device (device address), or null when the checks are off or
+// the address cannot be obtained (device_checks.hip).
+unsigned int *device_check_flags();
+// Synchronises the current device, returns its flags word and clears it (0 when the checks
+// are off); a HIP error code or 0.
+int read_and_clear_check_flags(uint32_t *flags);
 
 // Host helpers (pa_host.cpp).
 pa_status set_error(pa_status s, const char *fmt, ...);
+int max_len_of(const pa_decode_args *a);
 pa_status validate_decode(const pa_decode_args *a, bool need_device_pointers);
 pa_status plan_decode(const pa_decode_args *a, pa_plan *plan);
 pa_status make_decode_launch(const pa_decode_args *a, const pa_plan &plan, DecodeLaunch *L);

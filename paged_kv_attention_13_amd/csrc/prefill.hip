@@ -42,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "checks.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -109,8 +110,8 @@ __device__ int piece_tiles(const PrefillLaunch &p, int lane, int units_per_qtile
   for (int r0 = 0; r0 < p.num_rows; r0 += 64) {
     const int r = p.first_row + r0 + lane;
     if (r0 + lane < p.num_rows) {
-      const int L = p.seq_lens[r];
-      const int n = p.q_start_loc[r + 1] - p.q_start_loc[r];
+      const int L = checked_len(p.seq_lens[r], p.max_len, p.check_flags);
+      const int n = checked_qlen(p.q_start_loc[r + 1] - p.q_start_loc[r], L, p.check_flags);
       const int nq = (n + QB - 1) / QB;
       mx = max(mx, (L + KT - 1) / KT);
       work += (int64_t)nq * ((2 * (int64_t)(L - n) + n + QB) / KT + 2);

@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "checks.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -198,7 +199,7 @@ void verify_kernel(VerifyLaunch p) {
   // tokens each item covers (a group's shared prefix may be empty: no tiles)
   auto len_of = [&](int r) -> int {
     if constexpr (PREFIX) return p.shared_len[p.group_start[r]];
-    else return p.seq_lens[p.first_row + r];
+    else return checked_len(p.seq_lens[p.first_row + r], p.max_len, p.check_flags);
   };
 
   // Each unit counts unit_cost extra virtual tiles ahead of its real ones: starting a
@@ -290,9 +291,16 @@ void verify_kernel(VerifyLaunch p) {
     }
     const bool whole = !PREFIX && t0 == 0 && cnt == nb;
     // decode rows have one query each, at their own row index
+#if PA_DEVICE_CHECKS
+    int qbase = ITEM == kItemVerify ? p.q_start_loc[row] : row;
+    int n = ITEM == kItemVerify ? p.q_start_loc[row + 1] - qbase
+          : ITEM == kItemPrefix ? p.group_start[rb + 1] - row : 1;
+    if (ITEM == kItemVerify) checked_qrange(qbase, n, L, p.total_q, p.check_flags);
+#else
     const int qbase = ITEM == kItemVerify ? p.q_start_loc[row] : row;
     const int n = ITEM == kItemVerify ? p.q_start_loc[row + 1] - qbase
                 : ITEM == kItemPrefix ? p.group_start[rb + 1] - row : 1;
+#endif
     const int ncols = n << log2G;
     const int tok_begin = t0 * TILE;
     const int tok_end = min((t0 + cnt) * TILE, L);
@@ -350,7 +358,7 @@ void verify_kernel(VerifyLaunch p) {
       for (int tb = 0; tb < 2; ++tb) {
         const int tok0 = ts + 16 * tb;     // 16 tokens inside one page (bs >= 16)
         const int page = min(tok0 >> log2bs, last_page);
-        const int phys = __builtin_amdgcn_readlane(tbl, page - chunk_base);
+        const int phys = checked_block(__builtin_amdgcn_readlane(tbl, page - chunk_base), p.num_blocks, p.check_flags);
         const char *kp = kpool + (size_t)phys * phys_stride;
         vbase[tb] = vpool + (size_t)phys * phys_stride;
         const uint32_t krow = (uint32_t)(((tok0 + lq) & (bs - 1)) * (D * EB));
@@ -626,8 +634,15 @@ __global__ __launch_bounds__(64) void verify_merge_kernel(VerifyLaunch p) {
   const int rb = u / Hkv;
   const int g = u % Hkv;
   const int row = p.first_row + rb;
+#if PA_DEVICE_CHECKS
+  int qbase = ITEM == kItemDecode ? row : p.q_start_loc[row];
+  int n = ITEM == kItemDecode ? 1 : p.q_start_loc[row + 1] - qbase;
+  if (ITEM != kItemDecode)
+    checked_qrange(qbase, n, checked_len(p.seq_lens[row], p.max_len, p.check_flags), p.total_q, p.check_flags);
+#else
   const int qbase = ITEM == kItemDecode ? row : p.q_start_loc[row];
   const int n = ITEM == kItemDecode ? 1 : p.q_start_loc[row + 1] - qbase;
+#endif
   if (c >= n * G) return;
   int cnt = p.seg_count[u];
   if (cnt <= 1) return;                    // written directly by its only worker

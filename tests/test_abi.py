@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol(b):
 
 
 def test_abi_version(b):
-    assert b.LIB.pa_abi_version() == 3
+    assert b.LIB.pa_abi_version() == 4
 
 
 def test_struct_layout_matches_header(b):
@@ -757,3 +757,21 @@ def test_gather_probe_rejects_bad_arguments(b):
              ((0x10000, 0x10000, 4, 2048, 0x10000, 4, 3), "PA_ERR_UNSUPPORTED")]
     for args, status in cases:
         assert b.STATUS_NAMES[f(*args, None)] == status, args
+
+
+def test_device_checks_only_in_the_debug_build(b):
+    """The library reports its checks off and no flags without touching a device; the debug
+    build (PA_DEVICE_CHECKS=1) exports the same calls and reports its checks on."""
+    import ctypes as ct
+    assert b.LIB.pa_device_checks() == 0
+    assert b.device_check_flags() == 0
+    assert b.STATUS_NAMES[b.LIB.pa_device_check_flags(None)] == "PA_ERR_NULL_POINTER"
+    if os.path.basename(b.LIB_PATH).startswith("libpa_host"):
+        return                               # the host-only (sanitizer) build: no HIP library here
+    path = os.path.join(os.path.dirname(b.LIB_PATH), "libpa_kv_checked.so")
+    assert os.path.exists(path), "build() also builds libpa_kv_checked.so"
+    lib = ct.CDLL(path)
+    lib.pa_device_checks.restype = ct.c_int
+    assert lib.pa_device_checks() == 1
+    lib.pa_abi_version.restype = ct.c_int
+    assert lib.pa_abi_version() == b.LIB.pa_abi_version()
