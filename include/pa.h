@@ -242,7 +242,7 @@ size_t pa_decode_workspace_size(const pa_decode_args *a);
 /* Workspace bytes a pa_mixed call needs: its decode rows' split-K partials, its
  * verify rows' partials and, when the prefill rows make at most 256 (row, kv
  * head, head block, 32- to 128-position query tile) units, their kv pieces:
- * up to 4 per unit, each 4 x 32 x (128 + 2) fp32. */
+ * up to 8 per unit, each 4 x 32 x (128 + 2) fp32. */
 pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes);
 
 /* Decode attention over the paged cache: the decode kernel followed by the
@@ -303,7 +303,7 @@ pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
  * prefill-chunk rows through the MFMA causal tile kernel (bf16 q and KV), all
  * on `stream`.  The workspace (pa_mixed_workspace_size) holds the decode rows'
  * split records and partials, then the verify rows', then the prefill pieces
- * (a launch of few units cuts long units' cached context into up to 4 pieces
+ * (a launch of few units cuts long units' cached context into up to 8 pieces
  * and a merge kernel, also on the prefill stream, combines them). */
 pa_status pa_mixed(const pa_mixed_args *a, void *stream);
 

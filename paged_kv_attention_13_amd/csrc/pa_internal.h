@@ -45,7 +45,7 @@ inline int unit_max_units(int cus) { return cus * 2; }
 constexpr int unit_waves(int kv_dtype, int group) { return (kv_dtype == PA_F32 || group >= 8) ? 4 : 8; }
 constexpr int kPrefillTile = 64;         // prefill kernel: kv tokens per tile
 inline int prefill_slots(int cus) { return cus * 2; }   // prefill workgroups resident at once (2 per CU)
-constexpr int kPrefillMaxSplits = 4;     // prefill: at most this many kv pieces per unit
+constexpr int kPrefillMaxSplits = 8;     // prefill: at most this many kv pieces per unit
 constexpr int kPrefillMinChunkTiles = 4; // prefill: a piece covers at least this many tiles
 constexpr int kPrefillWaves = 4;         // prefill: waves per workgroup, 32 query positions each
 

@@ -14,7 +14,7 @@
 //
 // Tiling.  A workgroup (4 x wave64) owns one (row, kv head, block of query
 // heads, query tile) unit -- or, when the launch has at most 256 units, one kv
-// piece of it (the unit's tiles cut into up to 4 pieces whose partials the
+// piece of it (the unit's tiles cut into up to 8 pieces whose partials the
 // merge kernel combines); query tiles are dispatched longest first.  Each wave
 // owns 32 query positions of one query head.
 // K/V are staged through two LDS buffers in tiles of 64 tokens gathered page
@@ -99,8 +99,8 @@ __device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
 
 // Piece length (in kv tiles) of a split launch, the same in every wave of the prefill
 // kernel and of its merge: at least ceil(longest row's tiles / splits), so the launch's
-// `splits` pieces per unit always cover the unit, and at least 1.25 x the average work
-// per resident workgroup, so that a launch whose units are already balanced is not cut
+// `splits` pieces per unit always cover the unit, and at least the average work per
+// resident workgroup, so that a launch whose units are already balanced is not cut
 // further.  The work estimate per row takes its query tiles' mean visible length.
 template <int QB>
 __device__ int piece_tiles(const PrefillLaunch &p, int lane, int units_per_qtile) {
@@ -124,7 +124,7 @@ __device__ int piece_tiles(const PrefillLaunch &p, int lane, int units_per_qtile
   }
   const int64_t total = work * units_per_qtile / 2;
   const int64_t slots = p.resident_slots;
-  const int balanced = (int)((5 * total + 4 * slots - 1) / (4 * slots));
+  const int balanced = (int)((total + slots - 1) / slots);
   return max(max((mx + p.splits - 1) / p.splits, balanced), kPrefillMinChunkTiles);
 }
 

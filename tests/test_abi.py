@@ -298,8 +298,8 @@ def test_mixed_workspace_holds_prefill_pieces(b):
     assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
     dec = b.plan(_args(b, num_seqs=1, max_blocks_per_seq=256, max_seq_len=4096)).workspace_bytes
     units = 3 * 8 * 1 * 1          # rows x kv heads x head blocks (group 4) x query tiles of 32
-    splits = min(4, -(-2 * 512 // units), max(1, (4096 // 64) // 4))
-    assert splits == 4
+    splits = min(8, -(-2 * 512 // units), max(1, (4096 // 64) // 4))
+    assert splits == 8
     slots = units * splits
     assert n.value == r256(dec) + r256(slots * 4 * 32 * 128 * 4) + r256(slots * 4 * 32 * 2 * 4)
     m.max_q_len = 4096                                        # 3 x 8 x 128 units > 512
