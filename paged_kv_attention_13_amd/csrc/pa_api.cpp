@@ -207,7 +207,8 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.scale = b.scale;
     P.splits = mp.prefill_splits;
     P.max_qtiles = mp.prefill_qtiles;
-    P.resident_slots = prefill_slots(mp.cus);
+    P.resident_slots = prefill_slots(mp.cus, mp.prefill_waves);
+    P.waves = mp.prefill_waves;
     if (mp.prefill_splits > 1) {
       char *ws = static_cast<char *>(b.workspace);
       P.part_o = reinterpret_cast<float *>(ws + mp.prefill_offset);

@@ -278,18 +278,31 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPla
   // more units the pieces' extra traffic costs more than the balance gains (and in a
   // mixed batch the prefill already runs hidden beside the decode rows).
   mp->prefill_splits = 1;
+  mp->prefill_waves = 4;
   mp->prefill_qtiles = 0;
   mp->prefill_offset = 0;
   mp->prefill_ml_offset = 0;
   mp->prefill_slots = 0;
   if (n_pre > 0) {
     const int hb = prefill_heads_per_block(G);
-    const int qb = prefill_queries_per_block(G);
+    auto units_of = [&](int waves) {
+      const int qb = prefill_queries_per_block(G, waves);
+      return (int64_t)n_pre * b.num_kv_heads * (G / hb) * ((a->max_q_len + qb - 1) / qb);
+    };
+    // prefill rows alone take the 8-wave shape when its units fill two or more rounds of its
+    // resident workgroups (then the CUs stay balanced) or few enough to be cut into pieces;
+    // otherwise, and beside decode or verify rows (whose kernel leaves room for the smaller
+    // workgroups), the 4-wave shape
+    const int64_t u8 = units_of(8);
+    const int s8 = prefill_slots(cus, 8);
+    const int waves = (n_pre == B && (u8 >= 2 * (int64_t)s8 || u8 <= s8 / 2)) ? 8 : 4;
+    mp->prefill_waves = waves;
+    const int qb = prefill_queries_per_block(G, waves);
     mp->prefill_qtiles = (a->max_q_len + qb - 1) / qb;
-    const int64_t units_upper = (int64_t)n_pre * b.num_kv_heads * (G / hb) * mp->prefill_qtiles;
-    const int64_t tiles_upper = (b.max_seq_len + kPrefillTile - 1) / kPrefillTile;
+    const int64_t units_upper = units_of(waves);
+    const int64_t tiles_upper = (b.max_seq_len + prefill_tile(waves) - 1) / prefill_tile(waves);
     int splits = 1;
-    const int slots = prefill_slots(cus);
+    const int slots = prefill_slots(cus, waves);
     if (units_upper <= slots / 2) {
       splits = (int)std::min<int64_t>(kPrefillMaxSplits, (2 * slots + units_upper - 1) / units_upper);
       splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, tiles_upper / kPrefillMinChunkTiles));
@@ -299,8 +312,8 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPla
       mp->prefill_slots = (size_t)units_upper * splits;
       mp->prefill_offset = round_up(total, 256);
       mp->prefill_ml_offset =
-          mp->prefill_offset + round_up(mp->prefill_slots * kPrefillWaves * 32 * kHeadDim * sizeof(float), 256);
-      total = mp->prefill_ml_offset + round_up(mp->prefill_slots * kPrefillWaves * 32 * 2 * sizeof(float), 256);
+          mp->prefill_offset + round_up(mp->prefill_slots * waves * 32 * kHeadDim * sizeof(float), 256);
+      total = mp->prefill_ml_offset + round_up(mp->prefill_slots * waves * 32 * 2 * sizeof(float), 256);
     }
   }
   mp->total_bytes = total;

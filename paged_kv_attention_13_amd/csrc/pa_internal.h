@@ -43,16 +43,18 @@ inline int unit_max_units(int cus) { return cus * 2; }
 // waves of that workgroup: 8, or 4 where the per-wave state is large (fp32 pools,
 // or 8 query heads per kv head), which then fits one wave per SIMD without spills
 constexpr int unit_waves(int kv_dtype, int group) { return (kv_dtype == PA_F32 || group >= 8) ? 4 : 8; }
-constexpr int kPrefillTile = 64;         // prefill kernel: kv tokens per tile
-inline int prefill_slots(int cus) { return cus * 2; }   // prefill workgroups resident at once (2 per CU)
+// Prefill workgroup shapes: 4 waves staging 64-token kv tiles, two workgroups per CU; or 8
+// waves staging 128-token tiles, one workgroup per CU (each staged tile and barrier serve twice
+// the queries).  Both compute 64-token sub-tiles.
+inline int prefill_tile(int waves) { return 16 * waves; }                       // kv tokens per staged tile
+inline int prefill_slots(int cus, int waves) { return waves == 4 ? cus * 2 : cus; }  // resident workgroups
 constexpr int kPrefillMaxSplits = 8;     // prefill: at most this many kv pieces per unit
 constexpr int kPrefillMinChunkTiles = 4; // prefill: a piece covers at least this many tiles
-constexpr int kPrefillWaves = 4;         // prefill: waves per workgroup, 32 query positions each
 
 // Prefill geometry for group size G: query heads per workgroup (HB) and query
 // positions per workgroup (QB); a unit is (row, kv head, head block, query tile).
 inline int prefill_heads_per_block(int G) { return G == 1 ? 1 : (G == 2 ? 2 : 4); }
-inline int prefill_queries_per_block(int G) { return 32 * (kPrefillWaves / prefill_heads_per_block(G)); }
+inline int prefill_queries_per_block(int G, int waves) { return 32 * (waves / prefill_heads_per_block(G)); }
 
 // Everything a decode launch needs, resolved on the host.
 struct DecodeLaunch {
@@ -133,8 +135,9 @@ struct PrefillLaunch {
   int splits;                    // 1 = no split
   int max_qtiles;                // ceil(max_q_len / QB)
   int resident_slots;            // prefill workgroups resident at once on the device
-  float *part_o;                 // [slot][4 waves][32 q][128] fp32, unnormalised
-  float *part_ml;                // [slot][4 waves][32 q][2] fp32: running max (log2 domain), sum
+  int waves;                     // workgroup shape: 4 or 8 waves (32 query positions each)
+  float *part_o;                 // [slot][waves][32 q][128] fp32, unnormalised
+  float *part_ml;                // [slot][waves][32 q][2] fp32: running max (log2 domain), sum
 };
 
 struct VerifyLaunch {
@@ -258,6 +261,7 @@ struct MixedPlan {
   int verify_workers = 0;
   size_t verify_offset = 0;
   int prefill_splits = 1;
+  int prefill_waves = 4;          // prefill workgroup shape (prefill_tile, prefill_slots)
   int prefill_qtiles = 0;
   size_t prefill_offset = 0;      // piece outputs
   size_t prefill_ml_offset = 0;   // piece (max, sum) pairs

@@ -12,17 +12,20 @@
 // section "The LLM Inference Bottleneck: Prefill vs. Decode"), so the two
 // contractions run on the matrix cores.
 //
-// Tiling.  A workgroup (4 x wave64) owns one (row, kv head, block of query
-// heads, query tile) unit -- or, when the launch has at most 256 units, one kv
-// piece of it (the unit's tiles cut into up to 8 pieces whose partials the
-// merge kernel combines); query tiles are dispatched longest first.  Each wave
-// owns 32 query positions of one query head.
-// K/V are staged through two LDS buffers in tiles of 64 tokens gathered page
-// by page through the block table: while tile j is computed, tile j+1 sits in
-// the other buffer and tile j+2's global loads are in flight; one barrier per
+// Tiling.  A workgroup owns one (row, kv head, block of query heads, query
+// tile) unit -- or, when the launch has few units, one kv piece of it (the
+// unit's tiles cut into up to 8 pieces whose partials the merge kernel
+// combines); query tiles are dispatched longest first.  Each wave owns 32
+// query positions of one query head.  Two workgroup shapes, chosen by the host
+// plan: 4 waves staging 64-token kv tiles (two workgroups per CU), or 8 waves
+// staging 128-token tiles (one per CU; each staged tile and each barrier serve
+// twice the queries, for launches of prefill rows alone).
+// K/V are staged through two LDS buffers in tiles gathered page by page
+// through the block table: while tile j is computed, tile j+1 sits in the
+// other buffer and tile j+2's global loads are in flight; one barrier per
 // tile.  Each loading thread holds 4 consecutive tokens of 8 head-dim
 // elements, so V^T is formed in registers (byte permutes) and written with
-// 8-byte LDS stores.  Per tile and wave:
+// 8-byte LDS stores.  Per 64-token sub-tile and wave:
 //   S^T = K Q^T   : 32 x v_mfma_f32_16x16x32_bf16  (A = K rows from LDS,
 //                   B = Q^T held in registers for the whole row)
 //   online softmax in fp32 (log2 domain, lazy rescale as in the decode kernel;
@@ -55,16 +58,21 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = kHeadDim;        // 128
-constexpr int KT = 64;             // kv tokens per tile
+constexpr int ST = 64;             // kv tokens per computed sub-tile
 constexpr int QW = 32;             // query positions per wave
-constexpr int NWP = 4;             // waves per workgroup
-constexpr int NTP = NWP * 64;
 constexpr int K_STRIDE = 272;      // bytes per K row in LDS (256 + 16 pad: conflict-free 16-B reads)
-constexpr int V_STRIDE = 144;      // bytes per V^T row in LDS (128 + 16 pad)
+// Workgroup shape NW (4 or 8 waves): kv tiles of KT = 16 NW tokens are staged (each thread
+// holds 4 tokens x 8 elements of K and of V), V^T rows of KT tokens plus 16 bytes of pad
+template <int NW>
+struct Shape {
+  static constexpr int KT = 16 * NW;
+  static constexpr int NT = NW * 64;
+  static constexpr int V_STRIDE = 2 * KT + 16;
+  static constexpr int CHUNKS = KT * kHeadDim * 2 / 16 / NT;   // 16-byte chunks per thread and tile: 4
+};
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kSlack = 8.0f;
-constexpr int CHUNKS = KT * D * 2 / 16 / NTP;   // 16-byte chunks per thread per tile (K or V): 4
 constexpr int kTblLds = 1024;      // block-table entries staged in LDS (longer ranges read global memory)
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
@@ -102,7 +110,7 @@ __device__ __forceinline__ void store4(void *out, size_t idx, f32x4 v) {
 // `splits` pieces per unit always cover the unit, and at least the average work per
 // resident workgroup, so that a launch whose units are already balanced is not cut
 // further.  The work estimate per row takes its query tiles' mean visible length.
-template <int QB>
+template <int QB, int KT>
 __device__ int piece_tiles(const PrefillLaunch &p, int lane, int units_per_qtile) {
   if (p.splits <= 1) return 1 << 30;
   int mx = 0;
@@ -168,11 +176,15 @@ __device__ __forceinline__ PrefillUnit prefill_unit(const PrefillLaunch &p, int 
 }
 
 // HB: query heads per workgroup (1, 2 or 4); the 4 waves cover HB heads x (4/HB) query sub-tiles.
-template <int HB, bool OUT_BF16>
-__global__ __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int HB, bool OUT_BF16, int NWP>
+__global__ __launch_bounds__(NWP * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillLaunch p) {
   constexpr int QSUB = NWP / HB;
   constexpr int QB = QW * QSUB;            // queries per workgroup
+  constexpr int KT = Shape<NWP>::KT;
+  constexpr int NTP = Shape<NWP>::NT;
+  constexpr int V_STRIDE = Shape<NWP>::V_STRIDE;
+  constexpr int CHUNKS = Shape<NWP>::CHUNKS;
 
   // two LDS buffers: tile j is computed from buffer j&1 while tile j+1 is stored to the other
   __shared__ __attribute__((aligned(16))) char s_k[2][KT * K_STRIDE];
@@ -196,7 +208,7 @@ void prefill_kernel(PrefillLaunch p) {
   const int n = p.q_start_loc[row + 1] - q_begin;
   // a split launch's piece length: its loads go out beside the row's metadata, before any
   // exit, so that the two share one round trip (chunk of 256 after 8,192: 66.5 -> 64.9 us)
-  const int C = p.splits > 1 ? __builtin_amdgcn_readfirstlane(piece_tiles<QB>(p, threadIdx.x & 63, Hkv * hblocks))
+  const int C = p.splits > 1 ? __builtin_amdgcn_readfirstlane(piece_tiles<QB, KT>(p, threadIdx.x & 63, Hkv * hblocks))
                              : 1 << 30;
   if (qt * QB >= n) return;                // whole workgroup: past this row's chunk
   const int L = p.seq_lens[row];
@@ -296,7 +308,10 @@ void prefill_kernel(PrefillLaunch p) {
     // 16-byte LDS reads at twice the bytes per clock of 8-byte ones).  Pairs are XOR-ed with
     // (d >> 4) & 7, the operand's 16-row block: conflict-free operand reads, two-way
     // conflicted stores under a 64-bank model.
-    const int vgrp = 16 * ((4 * (c_tq >> 3) + (c_tq & 3)) ^ ((c_dg >> 1) & 7)) + 8 * ((c_tq >> 2) & 1);
+    // (128-token tiles: the same within each 64-token half of the row)
+    const int cq = KT == 64 ? c_tq : c_tq & 15;
+    const int vgrp = (KT == 64 ? 0 : 128 * (c_tq >> 4)) + 16 * ((4 * (cq >> 3) + (cq & 3)) ^ ((c_dg >> 1) & 7)) +
+                     8 * ((cq >> 2) & 1);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const uint32_t lo01 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x05040100u);   // e=2w:   t0 t1
@@ -322,10 +337,11 @@ void prefill_kernel(PrefillLaunch p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) vt_lane[i] = lq * V_STRIDE + 16 * (lg ^ i);
 
-  auto compute = [&](int j) {
-    const char *kb = s_k[j & 1];
-    const char *vb = s_vt[j & 1];
-    const int kv0 = j * KT;
+  // sub-tile hs (64 tokens) of staged tile j
+  auto compute = [&](int j, int hs) {
+    const char *kb = s_k[j & 1] + ST * hs * K_STRIDE;
+    const char *vb = s_vt[j & 1] + 2 * ST * hs;
+    const int kv0 = j * KT + ST * hs;
     // ---- S^T = K Q^T ----
     f32x4 s[4][2];
 #pragma unroll
@@ -356,7 +372,7 @@ void prefill_kernel(PrefillLaunch p) {
     // ---- causal mask, online softmax (per query column) ----
     // the max is taken over the raw scores (the scale is positive) and the scale enters each
     // weight through one fused multiply-add: p = 2^(s * scale * log2(e) - m)
-    const bool diag = kv0 + KT - 1 > prior + q0;          // some element may be masked
+    const bool diag = kv0 + ST - 1 > prior + q0;          // some element may be masked
     float tmax[2];
 #pragma unroll
     for (int qt2 = 0; qt2 < 2; ++qt2) {
@@ -435,7 +451,11 @@ void prefill_kernel(PrefillLaunch p) {
   if (j_begin + 1 < j_end) load_regs(j_begin + 1);
   __syncthreads();
   for (int j = j_begin; j < j_end; ++j) {
-    if (wave_active && j * KT <= wave_last_pos) compute(j);   // else fully masked for this wave
+    // sub-tiles past a wave's last query are fully masked (written out without a loop: the
+    // 4-wave shape's registers come out 15 higher through a one-trip loop)
+    if (wave_active && j * KT <= wave_last_pos) compute(j, 0);
+    if constexpr (KT == 2 * ST)
+      if (wave_active && j * KT + ST <= wave_last_pos) compute(j, 1);
     if (j + 1 < j_end) {
       store_lds((j + 1) & 1);
       if (j + 2 < j_end) load_regs(j + 2);
@@ -497,8 +517,9 @@ void prefill_kernel(PrefillLaunch p) {
 // so four times as many workgroups keep loads in flight.  Lane c < 8 of a wave first
 // forms the normalised piece weights of its c-th position; then lane pairs take one
 // position each, 4 consecutive head-dim elements per lane, all four steps unrolled.
-template <int HB, bool OUT_BF16>
-__global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
+template <int HB, bool OUT_BF16, int NWP>
+__global__ __launch_bounds__(NWP * 64) void prefill_merge_kernel(PrefillLaunch p) {
+  constexpr int KT = Shape<NWP>::KT;
   constexpr int QSUB = NWP / HB;
   constexpr int QB = QW * QSUB;
   const int Hq = p.num_q_heads;
@@ -516,7 +537,7 @@ __global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
   const int n = p.q_start_loc[row + 1] - q_begin;
   const int L = p.seq_lens[row];
   const int tid = threadIdx.x;
-  const int C = __builtin_amdgcn_readfirstlane(piece_tiles<QB>(p, tid & 63, Hkv * hblocks));
+  const int C = __builtin_amdgcn_readfirstlane(piece_tiles<QB, KT>(p, tid & 63, Hkv * hblocks));
   if (qt * QB >= n) return;
   const int prior = L - n;
   const int ntile = (prior + min(qt * QB + QB, n) + KT - 1) / KT;
@@ -586,9 +607,9 @@ __global__ __launch_bounds__(NTP) void prefill_merge_kernel(PrefillLaunch p) {
   }
 }
 
-template <int HB>
-int launch_hb(const PrefillLaunch &P, hipStream_t st) {
-  constexpr int QB = QW * (NWP / HB);
+template <int HB, int NW>
+int launch_shape(const PrefillLaunch &P, hipStream_t st) {
+  constexpr int QB = QW * (NW / HB);
   const int G = P.num_q_heads / P.num_kv_heads;
   if (P.max_qtiles != (P.max_q_len + QB - 1) / QB || P.splits < 1 || P.splits > kPrefillMaxSplits ||
       (P.splits > 1 && (!P.part_o || !P.part_ml)))
@@ -599,25 +620,39 @@ int launch_hb(const PrefillLaunch &P, hipStream_t st) {
   if (nwg > INT32_MAX) return (int)hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
   if (P.out_dtype == PA_BF16)
-    hipLaunchKernelGGL((prefill_kernel<HB, true>), grid, dim3(NTP), 0, st, P);
+    hipLaunchKernelGGL((prefill_kernel<HB, true, NW>), grid, dim3(NW * 64), 0, st, P);
   else
-    hipLaunchKernelGGL((prefill_kernel<HB, false>), grid, dim3(NTP), 0, st, P);
+    hipLaunchKernelGGL((prefill_kernel<HB, false, NW>), grid, dim3(NW * 64), 0, st, P);
   return (int)hipGetLastError();
 }
 
-template <int HB>
-int launch_merge_hb(const PrefillLaunch &P, hipStream_t st) {
-  constexpr int QB = QW * (NWP / HB);
+template <int HB, int NW>
+int launch_merge_shape(const PrefillLaunch &P, hipStream_t st) {
+  constexpr int QB = QW * (NW / HB);
   const int G = P.num_q_heads / P.num_kv_heads;
   if (P.max_qtiles != (P.max_q_len + QB - 1) / QB || P.splits < 2 || P.splits > kPrefillMaxSplits ||
       !P.part_o || !P.part_ml)
     return (int)hipErrorInvalidValue;
   dim3 grid(P.max_qtiles * 4, P.num_kv_heads * (G / HB), P.num_rows);
   if (P.out_dtype == PA_BF16)
-    hipLaunchKernelGGL((prefill_merge_kernel<HB, true>), grid, dim3(NTP), 0, st, P);
+    hipLaunchKernelGGL((prefill_merge_kernel<HB, true, NW>), grid, dim3(NW * 64), 0, st, P);
   else
-    hipLaunchKernelGGL((prefill_merge_kernel<HB, false>), grid, dim3(NTP), 0, st, P);
+    hipLaunchKernelGGL((prefill_merge_kernel<HB, false, NW>), grid, dim3(NW * 64), 0, st, P);
   return (int)hipGetLastError();
+}
+
+template <int HB>
+int launch_hb(const PrefillLaunch &P, hipStream_t st) {
+  if (P.waves == 8) return launch_shape<HB, 8>(P, st);
+  if (P.waves == 4) return launch_shape<HB, 4>(P, st);
+  return (int)hipErrorInvalidValue;
+}
+
+template <int HB>
+int launch_merge_hb(const PrefillLaunch &P, hipStream_t st) {
+  if (P.waves == 8) return launch_merge_shape<HB, 8>(P, st);
+  if (P.waves == 4) return launch_merge_shape<HB, 4>(P, st);
+  return (int)hipErrorInvalidValue;
 }
 
 }  // namespace
