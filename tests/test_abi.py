@@ -311,6 +311,37 @@ def test_mixed_workspace_holds_prefill_pieces(b):
     assert n.value == b.plan(_args(b, num_seqs=1, max_blocks_per_seq=256, max_seq_len=128)).workspace_bytes
 
 
+def test_prefill_alone_workgroup_shape(b):
+    """Prefill rows alone take the 8-wave shape (64 query positions per workgroup at group 4,
+    128-token kv tiles, one workgroup per CU) when its units fill at least two rounds of its
+    256 resident workgroups or at most half a round (then cut into pieces: slots of 8 waves);
+    in between, and beside decode rows, the 4-wave shape."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    m = _mixed_args(b, num_decode_rows=0, num_verify_rows=0, max_verify_q_len=0, total_q=4 * 4096)
+    m.base.max_blocks_per_seq, m.base.max_seq_len = 256, 4096
+    n = ctypes.c_size_t()
+    # 4 rows x 8 kv heads x one 64-position tile = 32 units <= 128: 8 pieces of >= 4 tiles each
+    m.max_q_len = 8
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    slots = 32 * min(8, (2 * 256 + 31) // 32, (4096 // 128) // 4)
+    assert n.value == r256(slots * 8 * 32 * 128 * 4) + r256(slots * 8 * 32 * 2 * 4)
+    # 4 x 8 x 64 = 2,048 units >= 512: no pieces
+    m.max_q_len = 4096
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    assert n.value == 0
+    # 4 x 8 x 8 = 256 units of the 8-wave shape, in neither range: 4-wave shape, 4 x 8 x 16 = 512
+    # units on its 512 slots, no pieces
+    m.max_q_len = 512
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    assert n.value == 0
+    # the same few units beside a decode row: 4-wave shape, 3 x 8 x 1 = 24 units, pieces of 4 waves
+    m.num_decode_rows, m.max_q_len = 1, 8
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0
+    dec = b.plan(_args(b, num_seqs=1, max_blocks_per_seq=256, max_seq_len=4096)).workspace_bytes
+    slots = 24 * min(8, (2 * 512 + 23) // 24, (4096 // 64) // 4)
+    assert n.value == r256(dec) + r256(slots * 4 * 32 * 128 * 4) + r256(slots * 4 * 32 * 2 * 4)
+
+
 def _cascade_args(b, **kw):
     c = b.CascadeArgs()
     c.base = _args(b, num_seqs=4, max_seq_len=128)

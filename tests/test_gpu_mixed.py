@@ -114,6 +114,21 @@ def test_prefill_pieces_start_mid_page(bs, dec):
     compare(got, ref, 1e-2, what=f"prefill pieces bs{bs}")
 
 
+@pytest.mark.parametrize("bs", [16, 64])
+def test_prefill_both_workgroup_shapes(bs):
+    """Prefill rows alone run in the 8-wave shape (128-token kv tiles as two 64-token sub-tiles;
+    here 4 x 8 units, cut into pieces, and 8 x 8 x 8 units of eight 512-token chunks, uncut); beside
+    a decode row the same rows run in the 4-wave shape.  All against the oracle."""
+    _announce(f"prefill workgroup shapes, bs={bs}")
+    pre = [(3000, 40), (700, 64), (1500, 17), (90, 3)]
+    for dec in ([], [500]):
+        w = _mixed(dec, pre, bs=bs, seed=61 + bs)
+        compare(run_mixed(w, out_dtype="f32"), oracle.paged_attention_workload(w), 1e-2,
+                what=f"shape test, decode rows {dec}")
+    w = _mixed([], [(37 * i, 512) for i in range(8)], bs=bs, seed=67 + bs)     # 8 x 8 x 8 = 512 units
+    compare(run_mixed(w, out_dtype="f32"), oracle.paged_attention_workload(w), 1e-2, what="8 chunks of 512")
+
+
 def test_prefill_many_units_unsplit():
     """More units than resident workgroups: no kv split, longest query tiles first."""
     _announce("prefill, 3 rows x 1024 new tokens")
