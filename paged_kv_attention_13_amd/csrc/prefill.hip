@@ -376,16 +376,14 @@ void prefill_kernel(PrefillLaunch p) {
     float tmax[2];
 #pragma unroll
     for (int qt2 = 0; qt2 < 2; ++qt2) {
-      const int qi = q0 + 16 * qt2 + lq;
-      const int pos = prior + min(qi, n - 1);
       if (diag) {
+        // element (tt, i) is token kv0 + 16 tt + 4 lg + i: visible up to the column's position,
+        // i.e. while 16 tt + i <= lim (compared with constants: no per-element index arithmetic)
+        const int lim = prior + min(q0 + 16 * qt2 + lq, n - 1) - kv0 - 4 * lg;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = kv0 + 16 * tt + 4 * lg + i;
-            s[tt][qt2][i] = tok <= pos ? s[tt][qt2][i] : -__builtin_inff();
-          }
+          for (int i = 0; i < 4; ++i) s[tt][qt2][i] = 16 * tt + i <= lim ? s[tt][qt2][i] : -__builtin_inff();
       }
       float mx = -__builtin_inff();
 #pragma unroll
