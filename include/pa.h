@@ -240,9 +240,11 @@ pa_status pa_decode_plan(const pa_decode_args *a, pa_plan *plan);
 size_t pa_decode_workspace_size(const pa_decode_args *a);
 
 /* Workspace bytes a pa_mixed call needs: its decode rows' split-K partials, its
- * verify rows' partials and, when the prefill rows make at most 256 (row, kv
- * head, head block, 32- to 128-position query tile) units, their kv pieces:
- * up to 8 per unit, each 4 x 32 x (128 + 2) fp32. */
+ * verify rows' partials and, when the prefill rows make few (row, kv head, head
+ * block, query tile) units -- at most half as many as the prefill workgroups
+ * resident at once (2 per CU for the 4-wave workgroups, 1 for the 8-wave ones
+ * that prefill rows alone may use) -- their kv pieces: up to 8 per unit, each
+ * waves x 32 x (128 + 2) fp32. */
 pa_status pa_mixed_workspace_size(const pa_mixed_args *a, size_t *bytes);
 
 /* Decode attention over the paged cache: the decode kernel followed by the
