@@ -127,6 +127,9 @@ def test_prefill_both_workgroup_shapes(bs):
                 what=f"shape test, decode rows {dec}")
     w = _mixed([], [(37 * i, 512) for i in range(8)], bs=bs, seed=67 + bs)     # 8 x 8 x 8 = 512 units
     compare(run_mixed(w, out_dtype="f32"), oracle.paged_attention_workload(w), 1e-2, what="8 chunks of 512")
+    # group 8: two head blocks per kv head, 8 x 8 x 2 x 8 = 1,024 units of the 8-wave shape
+    w = _mixed([], [(37 * i, 512) for i in range(8)], bs=bs, hq=64, seed=71 + bs)
+    compare(run_mixed(w, out_dtype="f32"), oracle.paged_attention_workload(w), 1e-2, what="group 8, 8 x 512")
 
 
 def test_prefill_many_units_unsplit():
