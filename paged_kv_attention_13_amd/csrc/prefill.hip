@@ -448,24 +448,26 @@ void prefill_kernel(PrefillLaunch p) {
   store_lds(j_begin & 1);
   if (j_begin + 1 < j_end) load_regs(j_begin + 1);
   __syncthreads();
-  // 8-wave shape: waves 4..7 (the second wave of each SIMD) store the next tile before
-  // computing this one, the others after, so that the two waves of a SIMD, which leave each
-  // barrier together, do not reach the staging stores and the softmax at the same time (the
-  // 8,192-token prompt 520 -> 506 us; the buffer they fill was last read before the barrier)
-  const bool stage_first = NWP == 8 && wave >= 4;
-  for (int j = j_begin; j < j_end; ++j) {
-    if (stage_first && j + 1 < j_end) {
+  // The next tile goes to LDS (and the global loads of the one after are issued) after this
+  // tile's computation -- in the 8-wave shape between its two sub-tiles, which gives those loads
+  // half a tile more lead and moves the staging stores away from the barrier (the 8,192-token
+  // prompt 520 -> 507 us; staging first in half of the waves gave 510 us).  The buffer written
+  // was last read before the previous barrier.
+  auto stage = [&](int j) {
+    if (j + 1 < j_end) {
       store_lds((j + 1) & 1);
       if (j + 2 < j_end) load_regs(j + 2);
     }
+  };
+  for (int j = j_begin; j < j_end; ++j) {
     // sub-tiles past a wave's last query are fully masked (written out without a loop: the
     // 4-wave shape's registers come out 15 higher through a one-trip loop)
     if (wave_active && j * KT <= wave_last_pos) compute(j, 0);
-    if constexpr (KT == 2 * ST)
+    if constexpr (KT == 2 * ST) {
+      stage(j);
       if (wave_active && j * KT + ST <= wave_last_pos) compute(j, 1);
-    if (!stage_first && j + 1 < j_end) {
-      store_lds((j + 1) & 1);
-      if (j + 2 < j_end) load_regs(j + 2);
+    } else {
+      stage(j);
     }
     __syncthreads();
   }
