@@ -307,6 +307,36 @@ def test_stages_equal_one_call():
     assert torch.equal(out1, out2)
 
 
+@pytest.mark.parametrize("kv_fmt,workers", [("bf16", 37), ("fp8", 0)])
+def test_merge_on_a_foreign_workspace_stays_in_bounds(kv_fmt, workers):
+    """The merge reads each cut unit's (first worker, count) record from the workspace, and a
+    record that did not come from a partials call on that workspace is clamped to the launch's
+    slots: pa_merge_partials on random bytes completes (its outputs are meaningless), and the
+    library is sound afterwards (a partials call then the merge match the oracle)."""
+    _announce(f"merge on a foreign workspace: {kv_fmt} workers={workers}")
+    import torch
+    from paged_kv_attention_13_amd import binding
+    from paged_kv_attention_13_amd.device import to_device
+    w = _small([300, 1200, 64, 2500], kv_fmt=kv_fmt, seed=71)
+    d = to_device(w)
+    out = torch.empty(d["q"].shape, dtype=torch.float32, device="cuda")
+    a = binding.make_decode_args(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], w.scale,
+                                 max_seq_len=w.max_seq_len, k_scale=d["k_scale"], v_scale=d["v_scale"], out=out,
+                                 num_workers=workers)
+    pl = binding.plan(a)
+    assert pl.workspace_bytes > 0
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    ws = torch.randint(0, 256, (pl.workspace_bytes,), dtype=torch.uint8, device="cuda", generator=gen)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), pl.workspace_bytes
+    binding.merge_partials(a)
+    torch.cuda.synchronize()
+    binding.decode_partials(a)
+    binding.merge_partials(a)
+    torch.cuda.synchronize()
+    compare(out.cpu().numpy().astype(np.float64), oracle.paged_attention_workload(w),
+            TOL_FP8 if kv_fmt == "fp8" else 5e-3, what=f"{kv_fmt} after a foreign-workspace merge")
+
+
 def test_empty_batch_is_a_no_op():
     _announce("empty batch")
     import torch
