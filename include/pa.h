@@ -217,7 +217,7 @@ int pa_abi_version(void);
  * pages) of an fp32 or bf16 cache, at most 2C (row, kv head) units, run one
  * workgroup per unit whose waves combine their results in LDS: workspace_bytes
  * is 0 and num_workers reports those waves.  When S = min(C / units,
- * ceil(tiles / 4), 16) is at least 2 (tiles = ceil(max_seq_len / 16); at most C/2
+ * ceil(tiles / 4), 8) is at least 2 (tiles = ceil(max_seq_len / 16); at most C/2
  * units of more than 4 tiles: a unit's one workgroup would leave CUs idle), each
  * unit is instead cut over S workgroups; num_workers reports the S x units
  * pieces and the workspace takes the layout below with S x units in place of

@@ -166,11 +166,11 @@ def test_plan_choices(b):
     a = _args(b, num_seqs=40, max_seq_len=1024, max_blocks_per_seq=64)
     p = b.plan(a)
     assert p.num_workers == 40 * 8 * 8 and p.workspace_bytes == 0
-    # ... or, with fewer units than CUs, each unit cut over S = min(CUs / units, tiles / 4, 16)
-    # workgroups (24 units: S = 10), whose partials take the split layout with S x units slots
+    # ... or, with fewer units than CUs, each unit cut over S = min(CUs / units, tiles / 4, 8)
+    # workgroups (24 units: S = 8), whose partials take the split layout with S x units slots
     a = _args(b, num_seqs=3, max_seq_len=1024, max_blocks_per_seq=64)
     p = b.plan(a)
-    units, S = 3 * 8, 10
+    units, S = 3 * 8, 8
     slots = (units + units * S) * 4
     r256 = lambda x: (x + 255) // 256 * 256
     assert p.num_workers == units * S
