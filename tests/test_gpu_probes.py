@@ -4,8 +4,8 @@ Every probed query's output must equal, bit for bit, the V vector of its
 target slot, which encodes (physical block, kv head, slot) as small integers
 (tests/probes.py; tests/test_probes.py checks on the CPU that the oracle gives
 exactly these values).  Probes run with 8 kv heads and 4 query heads per kv
-head, 16- and 64-token blocks, the library's worker count and an explicit
-split, for every kernel that reads the cache: the decode kernels (bf16, fp32),
+head, 16- and 64-token blocks (the decode kernels also 32 and 128), the
+library's worker count and an explicit split, for every kernel that reads the cache: the decode kernels (bf16, fp32),
 the multi-query kernel (FP8 decode rows, verify rows, shared prefixes) and the
 prefill-chunk kernel; then at the full size of every named workload in the
 launch configuration the benchmark times.
@@ -63,6 +63,18 @@ LONG = [1, 17, 100, 513, 1000, 2049, 3001]      # balanced split with partials a
 def test_decode_probes(kv_fmt, bs, rows, workers):
     _announce(f"decode probes kv={kv_fmt} bs={bs} rows={rows} workers={workers}")
     w = _workload(SHORT if rows == "short" else LONG, bs=bs, kv_fmt=kv_fmt, seed=bs + workers)
+    _sweep(w, lambda w, d: run_decode(w, out_dtype="f32", num_workers=workers, dev=d),
+           what=f"decode {kv_fmt} bs{bs} {rows} W{workers}")
+
+
+@pytest.mark.parametrize("kv_fmt", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("bs", [32, 128])
+@pytest.mark.parametrize("rows,workers", [("short", 0), ("long", 0), ("long", 37)])
+def test_decode_probes_other_block_sizes(kv_fmt, bs, rows, workers):
+    """32- and 128-token blocks (page size and slot arithmetic), fp32 pools included."""
+    _announce(f"decode probes kv={kv_fmt} bs={bs} rows={rows} workers={workers}")
+    q_fmt = "f32" if kv_fmt == "f32" else "bf16"
+    w = _workload(SHORT if rows == "short" else LONG, bs=bs, kv_fmt=kv_fmt, q_fmt=q_fmt, seed=3 * bs + workers)
     _sweep(w, lambda w, d: run_decode(w, out_dtype="f32", num_workers=workers, dev=d),
            what=f"decode {kv_fmt} bs{bs} {rows} W{workers}")
 
