@@ -4,7 +4,7 @@ Every probed query's output must equal, bit for bit, the V vector of its
 target slot, which encodes (physical block, kv head, slot) as small integers
 (tests/probes.py; tests/test_probes.py checks on the CPU that the oracle gives
 exactly these values).  Probes run with 8 kv heads and 4 query heads per kv
-head, 16- and 64-token blocks (the decode kernels also 32 and 128), the
+head, 16-, 32-, 64- and 128-token blocks (the shared-prefix probes 16 and 64), the
 library's worker count and an explicit split, for every kernel that reads the cache: the decode kernels (bf16, fp32),
 the multi-query kernel (FP8 decode rows, verify rows, shared prefixes) and the
 prefill-chunk kernel; then at the full size of every named workload in the
@@ -89,7 +89,7 @@ def test_decode_probes_group_sizes(hq, hkv, kv_fmt):
 
 
 @pytest.mark.parametrize("kv_fmt", ["bf16", "fp8"])
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
 @pytest.mark.parametrize("workers", [0, 23])
 def test_verify_probes(kv_fmt, bs, workers):
     _announce(f"verify probes kv={kv_fmt} bs={bs} workers={workers}")
@@ -102,7 +102,7 @@ def test_verify_probes(kv_fmt, bs, workers):
            what=f"verify {kv_fmt} bs{bs} W{workers}")
 
 
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
 @pytest.mark.parametrize("workers", [0, 37, None])
 def test_mixed_prefill_probes(bs, workers):
     """Decode rows plus prefill-chunk rows whose kv pieces start in the middle of a page
