@@ -34,7 +34,7 @@ def _case(bs, seed):
     return _shared(groups, shared, own, prefix_ids=[0, 1, 2, 3, 4, 0], bs=bs, seed=seed)
 
 
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
 @pytest.mark.parametrize("workers", [0, 1, 7, 300])
 def test_cascade_ragged(bs, workers):
     _announce(f"cascade ragged bs={bs} workers={workers}")

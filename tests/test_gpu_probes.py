@@ -4,7 +4,7 @@ Every probed query's output must equal, bit for bit, the V vector of its
 target slot, which encodes (physical block, kv head, slot) as small integers
 (tests/probes.py; tests/test_probes.py checks on the CPU that the oracle gives
 exactly these values).  Probes run with 8 kv heads and 4 query heads per kv
-head, 16-, 32-, 64- and 128-token blocks (the shared-prefix probes 16 and 64), the
+head, 16-, 32-, 64- and 128-token blocks, the
 library's worker count and an explicit split, for every kernel that reads the cache: the decode kernels (bf16, fp32),
 the multi-query kernel (FP8 decode rows, verify rows, shared prefixes) and the
 prefill-chunk kernel; then at the full size of every named workload in the
@@ -125,7 +125,7 @@ def test_prefill_probes_many_units():
     _sweep(w, lambda w, d: run_mixed(w, dev=d), launches=4, what="prefill many units")
 
 
-@pytest.mark.parametrize("bs", [16, 64])
+@pytest.mark.parametrize("bs", [16, 32, 64, 128])
 @pytest.mark.parametrize("workers", [0, 7])
 def test_cascade_probes(bs, workers):
     _announce(f"cascade probes bs={bs} workers={workers}")
