@@ -125,6 +125,16 @@ def test_prefill_probes_many_units():
     _sweep(w, lambda w, d: run_mixed(w, dev=d), launches=4, what="prefill many units")
 
 
+def test_prefill_probes_table_beyond_lds():
+    """A prefill launch without kv pieces whose units visit more pages than the 1,024 block-table
+    entries staged in LDS (one kv head, 8,224 new tokens after 16,384 cached, 16-token blocks:
+    1,026 to 1,538 pages per unit; 257 units of 32 positions, more than half the resident
+    workgroups, so no pieces): every load takes its block id from the table in global memory."""
+    _announce("prefill probes, block table beyond the LDS staging")
+    w = _workload([16384 + 8224], [8224], bs=16, hq=4, hkv=1, seed=91)
+    _sweep(w, lambda w, d: run_mixed(w, out_dtype="f32", dev=d), launches=3, what="prefill table beyond LDS")
+
+
 @pytest.mark.parametrize("bs", [16, 32, 64, 128])
 @pytest.mark.parametrize("workers", [0, 7])
 def test_cascade_probes(bs, workers):
