@@ -301,9 +301,11 @@ pa_status pa_decode_partials(const pa_decode_args *a, void *stream);
 pa_status pa_merge_partials(const pa_decode_args *a, void *stream);
 
 /* Mixed in-flight batch: decode rows through the split-K decode kernels,
- * verify rows through the split-K MFMA multi-query kernels (bf16 q and KV),
- * prefill-chunk rows through the MFMA causal tile kernel (bf16 q and KV), all
- * on `stream`.  The workspace (pa_mixed_workspace_size) holds the decode rows'
+ * verify rows through the split-K MFMA multi-query kernels (bf16 q; bf16 or
+ * FP8-E4M3 KV), prefill-chunk rows through the MFMA causal tile kernel (bf16 q;
+ * bf16 or FP8-E4M3 KV, the codes widened exactly to bf16 as each tile is staged,
+ * k_scale folded into the softmax scale and v_scale applied to the output), all
+ * on `stream`; fp32 pools take decode rows only.  The workspace (pa_mixed_workspace_size) holds the decode rows'
  * split records and partials, then the verify rows', then the prefill pieces
  * (a launch of few units cuts long units' cached context into up to 8 pieces
  * and a merge kernel, also on the prefill stream, combines them). */

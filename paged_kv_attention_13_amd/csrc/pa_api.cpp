@@ -188,6 +188,9 @@ pa_status pa_mixed(const pa_mixed_args *a, void *stream) {
     P.q = b.q;
     P.k_pool = b.k_pool;
     P.v_pool = b.v_pool;
+    P.k_scale = b.k_scale;
+    P.v_scale = b.v_scale;
+    P.kv_dtype = b.kv_dtype;
     P.block_table = b.block_table;
     P.seq_lens = b.seq_lens;
     P.q_start_loc = a->q_start_loc;

@@ -242,8 +242,8 @@ pa_status plan_mixed(const pa_mixed_args *a, bool need_device_pointers, MixedPla
     if (a->max_q_len < 1 || a->max_q_len > b.max_seq_len)
       return set_error(PA_ERR_BAD_SHAPE, "max_q_len=%d outside [1, max_seq_len=%d]", a->max_q_len,
                        b.max_seq_len);
-    if (b.kv_dtype != PA_BF16)
-      return set_error(PA_ERR_UNSUPPORTED, "prefill-chunk rows need a bf16 KV cache and bf16 q");
+    if (b.kv_dtype == PA_F32 || b.q_dtype != PA_BF16)
+      return set_error(PA_ERR_UNSUPPORTED, "prefill-chunk rows need bf16 q and a bf16 or FP8 KV cache");
   }
   const int cus = device_cus();
   mp->cus = cus;

@@ -108,8 +108,11 @@ struct DecodeLaunch {
 
 struct PrefillLaunch {
   const void *q;                 // [total_q][Hq][D] bf16
-  const void *k_pool;
+  const void *k_pool;            // bf16 or FP8-E4M3 pools
   const void *v_pool;
+  const float *k_scale;          // [Hkv] FP8 pools: dequantisation scales (else unused)
+  const float *v_scale;
+  int kv_dtype;                  // PA_BF16 or PA_FP8_E4M3
   const int32_t *block_table;
   const int32_t *seq_lens;
   const int32_t *q_start_loc;

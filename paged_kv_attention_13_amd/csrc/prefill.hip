@@ -25,7 +25,11 @@
 // other buffer and tile j+2's global loads are in flight; one barrier per
 // tile.  Each loading thread holds 4 consecutive tokens of 8 head-dim
 // elements, so V^T is formed in registers (byte permutes) and written with
-// 8-byte LDS stores.  Per 64-token sub-tile and wave:
+// 8-byte LDS stores.  FP8-E4M3 pools (the per-head-scaled codes of "TensorRT-LLM,
+// in depth", section "Quantization: fewer bytes per weight and per cached token")
+// load 8 codes per token and thread and widen them exactly to bf16 before the
+// same staging; the K scale joins the softmax scale and the V scale multiplies
+// the output.  Per 64-token sub-tile and wave:
 //   S^T = K Q^T   : 32 x v_mfma_f32_16x16x32_bf16  (A = K rows from LDS,
 //                   B = Q^T held in registers for the whole row)
 //   online softmax in fp32 (log2 domain, lazy rescale as in the decode kernel;
@@ -93,6 +97,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float dot2_ones(uint32_t w, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), c,
                                          false);
+}
+
+// Eight E4M3 codes (FP8 pools) widened to eight bf16 values, exactly: every E4M3 value is a
+// bf16 value.  The pool's per-head scales are applied outside the products.
+__device__ __forceinline__ u32x4 widen_e4m3x8(u32x2 w) {
+  auto pair = [](uint32_t c, bool hi) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, false));
+  };
+  return u32x4{pair(w[0], false), pair(w[0], true), pair(w[1], false), pair(w[1], true)};
 }
 
 template <bool OUT_BF16>
@@ -176,7 +190,9 @@ __device__ __forceinline__ PrefillUnit prefill_unit(const PrefillLaunch &p, int 
 }
 
 // HB: query heads per workgroup (1, 2 or 4); the 4 waves cover HB heads x (4/HB) query sub-tiles.
-template <int HB, bool OUT_BF16, int NWP>
+// FP8: E4M3 pools, widened to bf16 as each tile is staged; k_scale[g] joins the softmax scale
+// and v_scale[g] multiplies the output (or the piece's unnormalised output).
+template <int HB, bool OUT_BF16, int NWP, bool FP8>
 __global__ __launch_bounds__(NWP * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillLaunch p) {
   constexpr int QSUB = NWP / HB;
@@ -248,16 +264,22 @@ void prefill_kernel(PrefillLaunch p) {
       }
     }
   }
-  const float qk_scale = p.scale * kLog2e;
+  float v_scale = 1.f;
+  float qk_scale = p.scale * kLog2e;
+  if constexpr (FP8) {
+    qk_scale *= p.k_scale[g];
+    v_scale = p.v_scale[g];
+  }
 
   // cooperative tile loads: thread -> 4 consecutive tokens 4*tq .. 4*tq+3, elements 8*dg .. 8*dg+7,
   // so each load instruction of a wave covers four whole 256-byte token rows
   const int bs = p.block_size;
   const int log2bs = __builtin_ctz(bs);
   const int32_t *trow = p.block_table + (size_t)row * p.max_blocks_per_seq;
+  constexpr int EBY = FP8 ? 1 : 2;           // bytes per cached element
   const size_t page_elems = (size_t)bs * D;
-  const __bf16 *kpool = static_cast<const __bf16 *>(p.k_pool) + (size_t)g * page_elems;
-  const __bf16 *vpool = static_cast<const __bf16 *>(p.v_pool) + (size_t)g * page_elems;
+  const char *kpool = static_cast<const char *>(p.k_pool) + (size_t)g * page_elems * EBY;
+  const char *vpool = static_cast<const char *>(p.v_pool) + (size_t)g * page_elems * EBY;
   const size_t phys_stride = (size_t)Hkv * page_elems;
   // thread -> (token quad c_tq, 16-byte chunk c_dg).  The quad index is a bit permutation of
   // tid >> 4 chosen so that the two 16-lane halves of each 32-lane half-wave take quads that
@@ -277,7 +299,10 @@ void prefill_kernel(PrefillLaunch p) {
     for (int i = tid; i < npages; i += NTP) s_tbl[i] = trow[page0 + i];
   __syncthreads();
 
+  // the next tile in registers until its LDS stores: 8 bf16 elements per register quad, or for
+  // FP8 pools the raw codes (widened only by the stores, so that no load is waited for early)
   u32x4 rk[CHUNKS], rv[CHUNKS];
+  u32x2 ck[CHUNKS], cv[CHUNKS];
   auto load_regs = [&](int j) {
     // the 4 tokens share one page (4 | bs)
     const int t_first = j * KT + 4 * c_tq;
@@ -287,21 +312,42 @@ void prefill_kernel(PrefillLaunch p) {
     const size_t base = (size_t)phys * phys_stride + (size_t)(t_first & (bs - 1)) * D + 8 * c_dg;
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i) {
-      if (t_first + i < L) {
-        rk[i] = *reinterpret_cast<const u32x4 *>(kpool + base + i * D);
-        rv[i] = *reinterpret_cast<const u32x4 *>(vpool + base + i * D);
+      if constexpr (FP8) {
+        if (t_first + i < L) {
+          ck[i] = *reinterpret_cast<const u32x2 *>(kpool + base + i * D);
+          cv[i] = *reinterpret_cast<const u32x2 *>(vpool + base + i * D);
+        } else {
+          ck[i] = u32x2{0u, 0u};             // code 0 is +0
+          cv[i] = u32x2{0u, 0u};
+        }
       } else {
-        rk[i] = u32x4{0u, 0u, 0u, 0u};
-        rv[i] = u32x4{0u, 0u, 0u, 0u};
+        if (t_first + i < L) {
+          rk[i] = *reinterpret_cast<const u32x4 *>(kpool + 2 * (base + i * D));
+          rv[i] = *reinterpret_cast<const u32x4 *>(vpool + 2 * (base + i * D));
+        } else {
+          rk[i] = u32x4{0u, 0u, 0u, 0u};
+          rv[i] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   };
   auto store_lds = [&](int buf) {
     char *kb = s_k[buf];
     char *vb = s_vt[buf];
+    u32x4 tk[CHUNKS], tv[CHUNKS];
+#pragma unroll
+    for (int i = 0; i < CHUNKS; ++i) {
+      if constexpr (FP8) {
+        tk[i] = widen_e4m3x8(ck[i]);
+        tv[i] = widen_e4m3x8(cv[i]);
+      } else {
+        tk[i] = rk[i];
+        tv[i] = rv[i];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CHUNKS; ++i)
-      *reinterpret_cast<u32x4 *>(kb + (4 * c_tq + i) * K_STRIDE + c_dg * 16) = rk[i];
+      *reinterpret_cast<u32x4 *>(kb + (4 * c_tq + i) * K_STRIDE + c_dg * 16) = tk[i];
     // V^T: for element d = 8*dg + e, the 4 tokens 4*tq .. +3 become one 8-byte half of row d's
     // 16-byte pair 4*(tq >> 3) + (tq & 3) (low half for tq & 4 clear): a pair holds an MFMA
     // operand's 8 k slots in order, so each operand is one 16-byte read (gfx950 serves
@@ -314,10 +360,10 @@ void prefill_kernel(PrefillLaunch p) {
                      8 * ((cq >> 2) & 1);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const uint32_t lo01 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x05040100u);   // e=2w:   t0 t1
-      const uint32_t lo23 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x05040100u);   //         t2 t3
-      const uint32_t hi01 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x07060302u);   // e=2w+1: t0 t1
-      const uint32_t hi23 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x07060302u);
+      const uint32_t lo01 = __builtin_amdgcn_perm(tv[1][w], tv[0][w], 0x05040100u);   // e=2w:   t0 t1
+      const uint32_t lo23 = __builtin_amdgcn_perm(tv[3][w], tv[2][w], 0x05040100u);   //         t2 t3
+      const uint32_t hi01 = __builtin_amdgcn_perm(tv[1][w], tv[0][w], 0x07060302u);   // e=2w+1: t0 t1
+      const uint32_t hi23 = __builtin_amdgcn_perm(tv[3][w], tv[2][w], 0x07060302u);
       *reinterpret_cast<u32x2 *>(vb + (8 * c_dg + 2 * w) * V_STRIDE + vgrp) = u32x2{lo01, lo23};
       *reinterpret_cast<u32x2 *>(vb + (8 * c_dg + 2 * w + 1) * V_STRIDE + vgrp) = u32x2{hi01, hi23};
     }
@@ -492,7 +538,7 @@ void prefill_kernel(PrefillLaunch p) {
       if (q0 + ql >= n) continue;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4 *>(po + ql * D + 16 * dt + 4 * lg) = o[dt][qt2];
+        *reinterpret_cast<f32x4 *>(po + ql * D + 16 * dt + 4 * lg) = FP8 ? o[dt][qt2] * v_scale : o[dt][qt2];
       if (lg == 0) *reinterpret_cast<float2 *>(pml + 2 * ql) = float2{m[qt2], lsum[qt2]};
     }
     return;
@@ -513,6 +559,7 @@ void prefill_kernel(PrefillLaunch p) {
       for (int i = 0; i < 4; ++i) {
         const float q = v[i] * r;
         v[i] = __builtin_fmaf(__builtin_fmaf(-l, q, v[i]), r, q);
+        if constexpr (FP8) v[i] *= v_scale;
       }
       store4<OUT_BF16>(p.out, base + 16 * dt + 4 * lg, v);
     }
@@ -628,10 +675,20 @@ int launch_shape(const PrefillLaunch &P, hipStream_t st) {
   const int64_t nwg = (int64_t)P.max_qtiles * P.num_kv_heads * (G / HB) * P.num_rows * P.splits;
   if (nwg > INT32_MAX) return (int)hipErrorInvalidValue;
   dim3 grid((unsigned)nwg);
-  if (P.out_dtype == PA_BF16)
-    hipLaunchKernelGGL((prefill_kernel<HB, true, NW>), grid, dim3(NW * 64), 0, st, P);
-  else
-    hipLaunchKernelGGL((prefill_kernel<HB, false, NW>), grid, dim3(NW * 64), 0, st, P);
+  if (P.kv_dtype == PA_FP8_E4M3) {
+    if (!P.k_scale || !P.v_scale) return (int)hipErrorInvalidValue;
+    if (P.out_dtype == PA_BF16)
+      hipLaunchKernelGGL((prefill_kernel<HB, true, NW, true>), grid, dim3(NW * 64), 0, st, P);
+    else
+      hipLaunchKernelGGL((prefill_kernel<HB, false, NW, true>), grid, dim3(NW * 64), 0, st, P);
+  } else if (P.kv_dtype == PA_BF16) {
+    if (P.out_dtype == PA_BF16)
+      hipLaunchKernelGGL((prefill_kernel<HB, true, NW, false>), grid, dim3(NW * 64), 0, st, P);
+    else
+      hipLaunchKernelGGL((prefill_kernel<HB, false, NW, false>), grid, dim3(NW * 64), 0, st, P);
+  } else {
+    return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

@@ -200,11 +200,15 @@ def test_mixed_validation(b):
     m.max_q_len = 0
     assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_BAD_SHAPE"
     m.max_q_len = 4
+    # prefill-chunk rows take bf16 q with a bf16 or FP8 cache: FP8 pools pass validation (the
+    # call then stops at the missing workspace), fp32 pools are rejected
     m.base.kv_dtype = 2
     m.base.k_scale = m.base.v_scale = 0x10000
-    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
-    m.base.kv_dtype = 1
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_WORKSPACE_TOO_SMALL"
+    m.base.kv_dtype = m.base.q_dtype = m.base.out_dtype = 0
     m.base.k_scale = m.base.v_scale = None
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
+    m.base.kv_dtype = m.base.q_dtype = m.base.out_dtype = 1
     m.q_start_loc = None
     assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_NULL_POINTER"
 
@@ -235,7 +239,7 @@ def test_mixed_verify_class_validation(b, kw, status):
     assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == status
 
 
-def test_mixed_verify_rows_take_bf16_or_fp8_kv(b):
+def test_mixed_rows_take_bf16_or_fp8_kv(b):
     m = _mixed_args(b, num_decode_rows=2, num_verify_rows=2)   # no prefill rows
     m.base.kv_dtype = b.PA_FP8_E4M3
     m.base.k_scale = m.base.v_scale = 0x10000
@@ -243,9 +247,10 @@ def test_mixed_verify_rows_take_bf16_or_fp8_kv(b):
     assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_WORKSPACE_TOO_SMALL"
     n = ctypes.c_size_t()
     assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0 and n.value > 0
-    # prefill rows still need a bf16 cache
+    # prefill-chunk rows too
     m.num_verify_rows = 1
-    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_UNSUPPORTED"
+    assert b.STATUS_NAMES[b.LIB.pa_mixed(ctypes.byref(m), None)] == "PA_ERR_WORKSPACE_TOO_SMALL"
+    assert b.LIB.pa_mixed_workspace_size(ctypes.byref(m), ctypes.byref(n)) == 0 and n.value > 0
 
 
 def test_mixed_group_bounds_verify_q_len(b):

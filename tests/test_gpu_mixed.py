@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 import pa_inputs
-from gpu_util import TOL_BF16, TOL_REL_L2, compare, run_mixed
+from gpu_util import TOL_BF16, TOL_FP8, TOL_REL_L2, compare, run_mixed
 
 pytestmark = pytest.mark.gpu
 
@@ -13,13 +13,13 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def _mixed(dec_lens, pre, bs=16, hq=32, hkv=8, seed=0, poison=True):
+def _mixed(dec_lens, pre, bs=16, hq=32, hkv=8, seed=0, poison=True, kv_fmt="bf16"):
     """dec_lens: decode-row lengths; pre: list of (prior, q_len) prefill rows."""
     L = list(dec_lens) + [p + n for p, n in pre]
     ql = [1] * len(dec_lens) + [n for _, n in pre]
     return pa_inputs.make_workload(name="mixed", seq_lens=L, q_lens=ql, num_q_heads=hq, num_kv_heads=hkv,
                                    head_dim=128, block_size=bs, seed=seed, extra_blocks=3,
-                                   poison_unused=poison)
+                                   poison_unused=poison, kv_fmt=kv_fmt)
 
 
 PRE = [(0, 1), (0, 5), (0, 64), (3, 29), (17, 33), (100, 64), (250, 130), (0, 256), (1000, 96)]
@@ -130,6 +130,20 @@ def test_prefill_both_workgroup_shapes(bs):
     # group 8: two head blocks per kv head, 8 x 8 x 2 x 8 = 1,024 units of the 8-wave shape
     w = _mixed([], [(37 * i, 512) for i in range(8)], bs=bs, hq=64, seed=71 + bs)
     compare(run_mixed(w, out_dtype="f32"), oracle.paged_attention_workload(w), 1e-2, what="group 8, 8 x 512")
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_fp8_kv_prefill_rows(bs):
+    """FP8-E4M3 pools (NaN codes in every unused slot): prefill-chunk rows beside decode rows
+    (4-wave shape), alone and cut into kv pieces, and alone with 512 uncut units (8-wave shape),
+    against the oracle fed the dequantised values."""
+    _announce(f"fp8 kv prefill rows, bs={bs}")
+    for dec in ([1, 300, 3000], []):
+        w = _mixed(dec, PRE, bs=bs, seed=81 + bs, kv_fmt="fp8")
+        compare(run_mixed(w, out_dtype="f32"), oracle.paged_attention_workload(w), TOL_FP8,
+                what=f"fp8 prefill, decode rows {dec}")
+    w = _mixed([], [(37 * i, 512) for i in range(8)], bs=bs, seed=83 + bs, kv_fmt="fp8")
+    compare(run_mixed(w, out_dtype="f32"), oracle.paged_attention_workload(w), TOL_FP8, what="fp8 8 chunks of 512")
 
 
 def test_prefill_many_units_unsplit():

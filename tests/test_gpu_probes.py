@@ -102,19 +102,21 @@ def test_verify_probes(kv_fmt, bs, workers):
            what=f"verify {kv_fmt} bs{bs} W{workers}")
 
 
+@pytest.mark.parametrize("kv_fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("bs", [16, 32, 64, 128])
 @pytest.mark.parametrize("workers", [0, 37, None])
-def test_mixed_prefill_probes(bs, workers):
+def test_mixed_prefill_probes(kv_fmt, bs, workers):
     """Decode rows plus prefill-chunk rows whose kv pieces start in the middle of a page
     (few units: the launch cuts long units into pieces), with the diagonal among the targets.
     workers None: the prefill rows alone."""
-    _announce(f"prefill probes bs={bs} workers={workers}")
+    _announce(f"prefill probes kv={kv_fmt} bs={bs} workers={workers}")
     dec = [1, 300, 3000] if workers is not None else []
     workers = workers or 0
     pre = [(0, 64), (100, 256), (1000, 40), (37, 5), (2500, 33)]
-    w = _workload(dec + [p + n for p, n in pre], [1] * len(dec) + [n for _, n in pre], bs=bs, seed=bs + workers + 9)
+    w = _workload(dec + [p + n for p, n in pre], [1] * len(dec) + [n for _, n in pre], bs=bs, kv_fmt=kv_fmt,
+                  seed=bs + workers + 9)
     _sweep(w, lambda w, d: run_mixed(w, out_dtype="f32", num_workers=workers, dev=d),
-           what=f"prefill bs{bs} W{workers}")
+           what=f"prefill {kv_fmt} bs{bs} W{workers}")
 
 
 def test_prefill_probes_many_units():
@@ -205,12 +207,14 @@ def test_fp8_decode_block_permutation_bit_identical(bs, workers):
     np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("kv_fmt", ["bf16", "fp8"])
 @pytest.mark.parametrize("bs", [16, 64])
 @pytest.mark.parametrize("dec", [[1, 300, 3000], []])
-def test_prefill_block_permutation_bit_identical(bs, dec):
-    _announce(f"prefill block permutation bs={bs} decode rows {dec}")
+def test_prefill_block_permutation_bit_identical(kv_fmt, bs, dec):
+    _announce(f"prefill block permutation kv={kv_fmt} bs={bs} decode rows {dec}")
     pre = [(0, 64), (100, 256), (1000, 40), (2500, 33)]
-    w = _workload(dec + [p + n for p, n in pre], [1] * len(dec) + [n for _, n in pre], bs=bs, seed=400 + bs)
+    w = _workload(dec + [p + n for p, n in pre], [1] * len(dec) + [n for _, n in pre], bs=bs, kv_fmt=kv_fmt,
+                  seed=400 + bs)
     a = run_mixed(w)
     b = run_mixed(_permuted(w, 11 + bs))
     np.testing.assert_array_equal(a, b)
